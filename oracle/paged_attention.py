@@ -1,0 +1,215 @@
+"""Plain fp64 CPU oracle for paged decode attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The HIP library never calls it and
+shares no code with it; the two meet only in the seeded input arrays.
+
+What it computes, with the passage each step follows:
+
+* Cache layout ``key_cache / value_cache [num_blocks, block_size,
+  num_kv_heads, head_size]`` -- "01. PagedAttention 详解" (vLLM learning
+  book), §3 (storage layout).
+* Logical position t of a sequence lives in physical block
+  ``block_table[t // block_size]`` at offset ``t % block_size`` --
+  "PagedAttention 机制" wiki, §5.3.4 (its conceptual paged_attention loop),
+  and the book's §3 figure (request A's tokens 0..47 over blocks 42, 17, 99).
+* Decode order: the new token's k/v are appended to the next free slot of the
+  last block, then q attends over all cached positions -- book §4, decode
+  phase. So with context length L the newest token sits at position L-1.
+* Attention for one query head: logits ``scale * (q . k_t)`` for t < L,
+  softmax over t, weighted sum of v_t. The wiki's §5.3.4 sketch scales by
+  1/sqrt(head_dim) but omits the exponentiation and normalisation, and the
+  book's §4 formula did not survive extraction; the standard softmax
+  attention is the reading taken here.
+* Query head h reads kv head ``h // (num_q_heads // num_kv_heads)``
+  (grouped-query attention; the book's self-check Q2 only uses GQA as a size
+  effect, so consecutive query heads sharing one kv head is a reading).
+* L = 0 leaves the output at zero (the wiki sketch starts from
+  ``zeros_like(query)`` and its loop body never runs).
+* Split-K recombination (the book's §4 and §9 say v2 splits long sequences
+  across partitions): each partition keeps (max, exp-sum, normalised output)
+  and the combine rescales by exp(m_p - M). This is an exact identity and is
+  provided so its algebra can be checked against the unsplit definition.
+
+Storage values arrive as uint16 bit patterns with a dtype tag; they are
+upcast exactly to float64. ``scale`` is the float32 value handed to the
+library, upcast. Results are float64 and unrounded.
+"""
+from __future__ import annotations
+
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "to_float64", "physical_slot", "slot_mapping", "cache_write",
+    "gather_positions", "decode", "decode_one", "attention_weights",
+    "decode_partitioned", "blocks_needed",
+]
+
+
+def to_float64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of fp16 / bf16 bit patterns to float64."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        # bf16 is the top half of an IEEE binary32.
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    """Blocks a sequence of ``num_tokens`` occupies (wiki §5.3.2 allocate rule)."""
+    return (int(num_tokens) + block_size - 1) // block_size
+
+
+def physical_slot(table_row: np.ndarray, position: int, block_size: int) -> int:
+    """Flat slot index of logical ``position``: block id times block size plus offset."""
+    position = int(position)
+    return int(table_row[position // block_size]) * block_size + position % block_size
+
+
+def slot_mapping(block_tables: np.ndarray, context_lens: np.ndarray,
+                 block_size: int) -> np.ndarray:
+    """Slot of each sequence's newest token (position L-1); -1 when L == 0."""
+    out = np.empty(len(context_lens), dtype=np.int32)
+    for s, L in enumerate(np.asarray(context_lens).tolist()):
+        out[s] = physical_slot(block_tables[s], L - 1, block_size) if L > 0 else -1
+    return out
+
+
+def cache_write(key_cache: np.ndarray, value_cache: np.ndarray,
+                k: np.ndarray, v: np.ndarray,
+                slots: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Return copies of the caches with token i's k/v stored at ``slots[i]``.
+
+    ``k, v`` are ``[num_tokens, num_kv_heads, head_size]`` bit patterns; a
+    negative slot means "no write" for that token. Slots must be distinct.
+    """
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    bs = kc.shape[1]
+    live = [int(x) for x in np.asarray(slots).tolist() if x >= 0]
+    assert len(live) == len(set(live)), "cache_write: duplicate slots"
+    for i, slot in enumerate(np.asarray(slots).tolist()):
+        if slot < 0:
+            continue
+        kc[slot // bs, slot % bs] = k[i]
+        vc[slot // bs, slot % bs] = v[i]
+    return kc, vc
+
+
+def gather_positions(cache: np.ndarray, table_row: np.ndarray, length: int,
+                     kv_head: int, dtype: str) -> np.ndarray:
+    """Rows ``cache[table[t // bs], t % bs, kv_head, :]`` for t < length, as float64."""
+    bs = cache.shape[1]
+    t = np.arange(int(length), dtype=np.int64)
+    blocks = np.asarray(table_row, dtype=np.int64)[t // bs]
+    return to_float64(cache[blocks, t % bs, kv_head, :], dtype)
+
+
+def _softmax_attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray,
+                    scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    logits = scale * (K @ qv)
+    m = logits.max()
+    w = np.exp(logits - m)
+    p = w / w.sum()
+    return p @ V, p
+
+
+def decode_one(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+               block_tables: np.ndarray, context_lens: np.ndarray, scale,
+               dtype: str, seq: int, head: int) -> np.ndarray:
+    """Output row ``out[seq, head, :]`` in float64."""
+    Hq = q.shape[1]
+    Hkv = key_cache.shape[2]
+    g = head // (Hq // Hkv)
+    L = int(context_lens[seq])
+    if L == 0:
+        return np.zeros(q.shape[2], dtype=np.float64)
+    K = gather_positions(key_cache, block_tables[seq], L, g, dtype)
+    V = gather_positions(value_cache, block_tables[seq], L, g, dtype)
+    qv = to_float64(q[seq, head], dtype)
+    out, _ = _softmax_attend(qv, K, V, float(np.float32(scale)))
+    return out
+
+
+def decode(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+           block_tables: np.ndarray, context_lens: np.ndarray, scale,
+           dtype: str, seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+    """``out[s, h, :] = softmax(scale * q[s,h] . K_g^T) V_g`` over positions < L_s.
+
+    Returns float64 ``[len(seqs), Hq, D]`` (all sequences by default). Each kv
+    head's rows are gathered once and reused by its query-head group.
+    """
+    B, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    G = Hq // Hkv
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    sc = float(np.float32(scale))
+    out = np.zeros((len(seqs), Hq, D), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        L = int(context_lens[s])
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            K = gather_positions(key_cache, block_tables[s], L, g, dtype)
+            V = gather_positions(value_cache, block_tables[s], L, g, dtype)
+            for h in range(g * G, (g + 1) * G):
+                out[i, h], _ = _softmax_attend(to_float64(q[s, h], dtype), K, V, sc)
+    return out
+
+
+def attention_weights(q: np.ndarray, key_cache: np.ndarray, block_tables: np.ndarray,
+                      context_lens: np.ndarray, scale, dtype: str,
+                      seq: int, head: int) -> np.ndarray:
+    """Softmax weights over positions < L for one (sequence, query head)."""
+    Hq = q.shape[1]
+    Hkv = key_cache.shape[2]
+    g = head // (Hq // Hkv)
+    L = int(context_lens[seq])
+    K = gather_positions(key_cache, block_tables[seq], L, g, dtype)
+    logits = float(np.float32(scale)) * (K @ to_float64(q[seq, head], dtype))
+    w = np.exp(logits - logits.max())
+    return w / w.sum()
+
+
+def decode_partitioned(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                       block_tables: np.ndarray, context_lens: np.ndarray, scale,
+                       dtype: str, partition_size: int,
+                       seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Same result as :func:`decode`, computed partition by partition.
+
+    Partition p covers positions [p*P, min((p+1)*P, L)). It keeps its own max
+    m_p, exp-sum Z_p and normalised output o_p; the combine takes
+    M = max m_p, c_p = Z_p * exp(m_p - M) and returns sum c_p o_p / sum c_p.
+    """
+    B, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    G = Hq // Hkv
+    P = int(partition_size)
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    sc = float(np.float32(scale))
+    out = np.zeros((len(seqs), Hq, D), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        L = int(context_lens[s])
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            K = gather_positions(key_cache, block_tables[s], L, g, dtype)
+            V = gather_positions(value_cache, block_tables[s], L, g, dtype)
+            for h in range(g * G, (g + 1) * G):
+                qv = to_float64(q[s, h], dtype)
+                parts: List[Tuple[float, float, np.ndarray]] = []
+                for a in range(0, L, P):
+                    logits = sc * (K[a:a + P] @ qv)
+                    m_p = logits.max()
+                    w = np.exp(logits - m_p)
+                    Z_p = w.sum()
+                    parts.append((m_p, Z_p, (w @ V[a:a + P]) / Z_p))
+                M = max(m for m, _, _ in parts)
+                c = np.array([Z * np.exp(m - M) for m, Z, _ in parts])
+                o = np.stack([o for _, _, o in parts])
+                out[i, h] = (c @ o) / c.sum()
+    return out

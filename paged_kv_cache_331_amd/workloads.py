@@ -1,0 +1,298 @@
+"""Seeded synthetic decode batches for paged attention.
+
+This module only *draws inputs*: context lengths, block tables over a shuffled
+physical pool, and N(0,1) query / key / value data rounded to the 2-byte
+storage type. It performs none of the attention arithmetic (no slot
+computation, no gather, no softmax), so the CPU oracle and the HIP path can
+both consume the very same arrays without sharing any of the method's code.
+
+Shapes follow the cache layout of "01. PagedAttention 详解" (vLLM learning
+book), §3: key_cache / value_cache are ``[num_blocks, block_size,
+num_kv_heads, head_size]``; block tables are one int32 row per sequence,
+packed into a single ``[num_seqs, max_blocks_per_seq]`` array (same page,
+§10, questions on how the table reaches the GPU and on a 100k-token table).
+A sequence of L tokens owns ceil(L / block_size) blocks ("PagedAttention 机制"
+wiki, §5.3.2, the allocation rule of its BlockTable sketch).
+
+Values are returned as numpy ``uint16`` bit patterns plus a dtype tag
+("fp16" / "bf16"); both sides upcast them with their own code.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+from typing import Optional, Sequence
+
+import numpy as np
+
+SEED_ROOT = 331
+# Elements per independently seeded chunk of a bulk normal draw. Fixed, so the
+# values do not depend on how many threads fill them.
+_CHUNK = 1 << 22
+# Seed-stream ids for the independent draws of one batch.
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_KNEW, _STREAM_VNEW = 1, 2, 3, 4, 5
+
+DTYPES = ("fp16", "bf16")
+
+
+@dataclass(frozen=True)
+class WorkloadSpec:
+    """Shape and length distribution of one synthetic decode batch."""
+
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    dtype: str
+    lengths: str                 # "uniform" | "lognormal"
+    len_lo: int                  # inclusive bounds (uniform) or clip bounds (lognormal)
+    len_hi: int
+    len_median: float = 0.0      # lognormal only
+    len_sigma: float = 1.0       # lognormal only
+    num_blocks: Optional[int] = None   # fixed pool size; None -> ceil(1.1 * blocks used)
+    shared_prefix_blocks: int = 0      # leading blocks common to every table
+    partition_size: int = 0            # split-K partition the workload is quoted with (0: auto)
+    cache_write: bool = True           # one new token per sequence written before attention
+    seed_index: int = 0                # second word of the seed key
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_len(self) -> int:
+        """Largest context length the distribution can produce."""
+        if self.shared_prefix_blocks:
+            return self.shared_prefix_blocks * self.block_size + self.len_hi
+        return self.len_hi
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return -(-self.max_len // self.block_size)
+
+
+# The five decode workloads, in order. Lengths count the new token, which is
+# written at position L-1 before the attention step reads positions [0, L)
+# (decode flow of "01. PagedAttention 详解", §4).
+CONFIGS = {
+    "tiny_write": WorkloadSpec(
+        name="tiny_write", num_seqs=4, num_q_heads=4, num_kv_heads=4, head_size=64,
+        block_size=16, dtype="fp16", lengths="uniform", len_lo=1, len_hi=100,
+        num_blocks=64, seed_index=1),
+    "llama2_7b_mha": WorkloadSpec(
+        name="llama2_7b_mha", num_seqs=64, num_q_heads=32, num_kv_heads=32, head_size=128,
+        block_size=16, dtype="fp16", lengths="uniform", len_lo=512, len_hi=2048,
+        seed_index=2),
+    "gqa_8b": WorkloadSpec(
+        name="gqa_8b", num_seqs=256, num_q_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, dtype="bf16", lengths="lognormal", len_lo=16, len_hi=4096,
+        len_median=1000.0, len_sigma=1.0, seed_index=3),
+    "long_context_splitk": WorkloadSpec(
+        name="long_context_splitk", num_seqs=4, num_q_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, dtype="fp16", lengths="uniform", len_lo=32768, len_hi=100000,
+        partition_size=512, seed_index=4),
+    "prefix_shared_write": WorkloadSpec(
+        name="prefix_shared_write", num_seqs=128, num_q_heads=32, num_kv_heads=8, head_size=128,
+        block_size=32, dtype="bf16", lengths="uniform", len_lo=16, len_hi=512,
+        shared_prefix_blocks=32, seed_index=5),
+}
+CONFIG_ORDER = ("tiny_write", "llama2_7b_mha", "gqa_8b", "long_context_splitk",
+                "prefix_shared_write")
+
+
+@dataclass
+class Batch:
+    """One decode batch: every array is host memory (numpy)."""
+
+    spec: WorkloadSpec
+    q: np.ndarray              # uint16 [B, Hq, D]
+    key_cache: np.ndarray      # uint16 [NB, bs, Hkv, D]
+    value_cache: np.ndarray    # uint16 [NB, bs, Hkv, D]
+    block_tables: np.ndarray   # int32 [B, MB]
+    context_lens: np.ndarray   # int32 [B]
+    k_new: np.ndarray          # uint16 [B, Hkv, D]  (the new token's key)
+    v_new: np.ndarray          # uint16 [B, Hkv, D]
+    scale: np.float32
+    used_blocks: np.ndarray    # int64 ids of physical blocks some table uses
+    pad_block: int             # id stored in table entries past a sequence's blocks
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def dtype(self) -> str:
+        return self.spec.dtype
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.extra.get("num_blocks", self.key_cache.shape[0]))
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> 2-byte storage bits, round to nearest even (finite inputs)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        u = x.view(np.uint32)
+        return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def nan_bits(dtype: str) -> int:
+    """A quiet-NaN bit pattern of the storage type (used to poison memory)."""
+    return {"fp16": 0x7E00, "bf16": 0x7FC0}[dtype]
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fill_normal(shape: Sequence[int], dtype: str, key: Sequence[int]) -> np.ndarray:
+    """N(0,1) float32 draws rounded to ``dtype``, as uint16 bits.
+
+    The array is cut into fixed chunks of ``_CHUNK`` elements; chunk i draws
+    from ``SeedSequence(key).spawn(...)[i]``, so the result depends only on
+    ``key`` and ``shape``.
+    """
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+    nch = -(-n // _CHUNK)
+    if nch == 0:
+        return out.reshape(shape)
+    kids = np.random.SeedSequence(list(key)).spawn(nch)
+
+    def work(i: int) -> None:
+        a = i * _CHUNK
+        b = min(n, a + _CHUNK)
+        x = np.random.default_rng(kids[i]).standard_normal(b - a, dtype=np.float32)
+        out[a:b] = round_to_storage(x, dtype)
+
+    if nch == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nch)))
+    return out.reshape(shape)
+
+
+def draw_lengths(spec: WorkloadSpec, rng: np.random.Generator, num_seqs: int) -> np.ndarray:
+    """Context lengths (including the new token), int32 [num_seqs]."""
+    if spec.lengths == "uniform":
+        lens = rng.integers(spec.len_lo, spec.len_hi, size=num_seqs, endpoint=True)
+    elif spec.lengths == "lognormal":
+        z = rng.standard_normal(num_seqs)
+        lens = np.rint(np.exp(math.log(spec.len_median) + spec.len_sigma * z))
+        lens = np.clip(lens, spec.len_lo, spec.len_hi)
+    else:
+        raise ValueError(spec.lengths)
+    lens = lens.astype(np.int64)
+    if spec.shared_prefix_blocks:
+        lens = lens + spec.shared_prefix_blocks * spec.block_size
+    return lens.astype(np.int32)
+
+
+def make_batch(spec: WorkloadSpec, *, lengths: Optional[Sequence[int]] = None,
+               num_seqs: Optional[int] = None, seed: Optional[Sequence[int]] = None,
+               max_blocks_per_seq: Optional[int] = None, values: bool = True) -> Batch:
+    """Draw one batch for ``spec``.
+
+    Draw order: lengths, then the pool permutation (both from
+    ``default_rng([331, seed_index])``), then q, K pool, V pool, new k, new v
+    (each from its own seed stream). ``lengths`` overrides the length draw
+    (edge-case tests); ``num_seqs`` shrinks the batch. ``values=False`` draws
+    only lengths and tables (the value arrays come back empty).
+    """
+    key = list(seed) if seed is not None else [SEED_ROOT, spec.seed_index]
+    rng = np.random.default_rng(key)
+    if lengths is not None:
+        lens = np.asarray(lengths, dtype=np.int32)
+    else:
+        lens = draw_lengths(spec, rng, num_seqs if num_seqs is not None else spec.num_seqs)
+    B = int(lens.shape[0])
+    bs = spec.block_size
+    if np.any(lens < 0):
+        raise ValueError("negative context length")
+
+    nblk = (lens.astype(np.int64) + bs - 1) // bs          # blocks each sequence owns
+    shared = spec.shared_prefix_blocks
+    if shared and B and np.any(nblk < shared):
+        raise ValueError("a sequence is shorter than the shared prefix")
+    private = nblk - shared if shared else nblk
+    distinct = int(private.sum()) + (shared if B else 0)
+
+    if spec.num_blocks is not None:
+        NB = spec.num_blocks
+        if NB < distinct + 1:
+            raise ValueError("fixed pool too small")
+    else:
+        NB = max(distinct + 1, int(math.ceil(1.1 * distinct)))
+    MB = max_blocks_per_seq if max_blocks_per_seq is not None else max(
+        spec.max_blocks_per_seq, int(nblk.max()) if B else 1)
+    if B and int(nblk.max()) > MB:
+        raise ValueError("max_blocks_per_seq too small")
+
+    perm = rng.permutation(NB).astype(np.int64)
+    pad_block = int(perm[distinct])            # never used by any sequence
+    tables = np.full((B, MB), pad_block, dtype=np.int32)
+    cursor = 0
+    prefix = perm[:shared] if shared else perm[:0]
+    cursor += shared if B else 0
+    for s in range(B):
+        row = []
+        if shared:
+            row.extend(prefix.tolist())
+        n = int(private[s])
+        row.extend(perm[cursor:cursor + n].tolist())
+        cursor += n
+        tables[s, :len(row)] = row
+    used = perm[:distinct].copy()
+
+    Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_size
+    dt = spec.dtype
+    if values:
+        q = fill_normal((B, Hq, D), dt, key + [_STREAM_Q])
+        kc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_K])
+        vc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_V])
+        k_new = fill_normal((B, Hkv, D), dt, key + [_STREAM_KNEW])
+        v_new = fill_normal((B, Hkv, D), dt, key + [_STREAM_VNEW])
+    else:
+        q = np.empty((0, Hq, D), np.uint16)
+        kc = vc = np.empty((0, bs, Hkv, D), np.uint16)
+        k_new = v_new = np.empty((0, Hkv, D), np.uint16)
+    scale = np.float32(1.0 / math.sqrt(D))
+    return Batch(spec=spec, q=q, key_cache=kc, value_cache=vc, block_tables=tables,
+                 context_lens=lens, k_new=k_new, v_new=v_new, scale=scale,
+                 used_blocks=used, pad_block=pad_block, extra={"num_blocks": NB})
+
+
+def small_variant(name: str, num_seqs: int) -> WorkloadSpec:
+    """A config with fewer sequences (same shapes and length law)."""
+    return replace(CONFIGS[name], num_seqs=num_seqs)
+
+
+def poison_unused_blocks(batch: Batch) -> None:
+    """Fill every physical block no table uses (including the pad block) with NaN."""
+    mask = np.ones(batch.num_blocks, dtype=bool)
+    mask[batch.used_blocks] = False
+    nb = nan_bits(batch.dtype)
+    batch.key_cache[mask] = nb
+    batch.value_cache[mask] = nb

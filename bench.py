@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step is one pass of the whole decode hot path over a synthetic batch
+already resident in HBM: the newest token's slot (pa_decode_slot_mapping),
+the cache write of its k/v (pa_cache_write), then paged attention over every
+cached position (pa_decode, automatic single-pass / split-K choice).
+
+Default workload: the Llama-2-7B-shaped single-layer decode batch (64
+sequences, 32 query = 32 kv heads, head size 128, block size 16, fp16,
+context lengths uniform in [512, 2048], shuffled block tables over a pool of
+the blocks used plus 10%).
+
+Prints ONE JSON line: tokens/s for the whole job (one new token per sequence
+per step), the decode kernel's achieved HBM bandwidth against MI355X's 8 TB/s
+peak (from HIP events recorded on the launch stream inside the timed
+region), and the fp64 CPU oracle timed on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
+METRIC = "decode attn tokens/s + effective KV HBM GB/s (% of MI355X peak), 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = ("paged_kv_cache_331_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_331_amd/csrc/pa_device.h")
+
+
+def algorithmic_bytes(spec, context_lens: np.ndarray) -> dict:
+    """Bytes the decode step must move at least once.
+
+    Per (token, kv head): K and V rows, 2 * head_size * 2 bytes. Plus q and
+    out (num_seqs * num_q_heads * head_size * 2 bytes each), the table entries
+    actually used (4 bytes per block) and the lengths (4 bytes per sequence).
+    Positions >= L and split-K scratch are overhead, not counted.
+    """
+    L = context_lens.astype(np.int64)
+    esz = 2
+    per_token_head = 2 * spec.head_size * esz
+    kv = int(L.sum()) * spec.num_kv_heads * per_token_head
+    if spec.shared_prefix_blocks:
+        pre = spec.shared_prefix_blocks * spec.block_size
+        kv_unique = (int((L - pre).sum()) + pre) * spec.num_kv_heads * per_token_head
+    else:
+        kv_unique = kv
+    qo = 2 * len(L) * spec.num_q_heads * spec.head_size * esz
+    tables = int(((L + spec.block_size - 1) // spec.block_size).sum()) * 4
+    lens = 4 * len(L)
+    return {"kv": kv, "kv_unique": kv_unique, "q_out": qo, "tables": tables, "lens": lens,
+            "total": kv + qo + tables + lens,
+            "total_unique": kv_unique + qo + tables + lens,
+            "per_token_head": per_token_head}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Counter-measured HBM traffic per decode launch, if taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(batch, budget_s: float) -> dict:
+    """Time the fp64 oracle (as it stands) on a prefix of the batch's sequences."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        for s in range(batch.num_seqs):
+            oracle.slot_mapping(batch.block_tables[s:s + 1], batch.context_lens[s:s + 1],
+                                batch.spec.block_size)
+            oracle.decode(batch.q, batch.key_cache, batch.value_cache, batch.block_tables,
+                          batch.context_lens, batch.scale, batch.dtype, seqs=[s])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle (slot of the newest token + attention, single "
+                       f"thread) over the first {done} of {batch.num_seqs} sequences of the "
+                       f"same batch, {dt:.1f} s; one decoded token per sequence")}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2_7b_mha")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="0 automatic, <0 single pass, >0 split-K partition tokens")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 to skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("steps must be >= 1 and warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_kv_cache_331_amd import pa, workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    pa.load()          # the HIP library must be built; there is no fallback
+    spec = wl.CONFIGS[args.workload]
+    print(f"# generating {spec.name}", file=sys.stderr, flush=True)
+    batch = wl.make_batch(spec)
+    tdt = torch.float16 if spec.dtype == "fp16" else torch.bfloat16
+
+    def up16(a):
+        return torch.from_numpy(a.view(np.int16)).view(tdt).cuda()
+
+    q, kc, vc = up16(batch.q), up16(batch.key_cache), up16(batch.value_cache)
+    k_new, v_new = up16(batch.k_new), up16(batch.v_new)
+    bt = torch.from_numpy(batch.block_tables).cuda()
+    lens = torch.from_numpy(batch.context_lens).cuda()
+    out = torch.empty_like(q)
+    slots = torch.empty(batch.num_seqs, dtype=torch.int32, device="cuda")
+    maxlen = batch.max_context_len
+    ws_bytes = pa.decode_workspace_size(batch.num_seqs, spec.num_q_heads, spec.head_size,
+                                        maxlen, args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    scale = float(batch.scale)
+    stream = torch.cuda.current_stream()
+
+    def step(ev0=None, ev1=None):
+        pa.decode_slot_mapping(bt, lens, spec.block_size, out=slots, stream=stream)
+        pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        pa.decode(q, kc, vc, bt, lens, scale, maxlen, out=out,
+                  partition_size=args.partition_size, workspace=ws, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    decode_ms = float(np.mean(dec_ms))
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode {decode_ms:.4f} ms",
+          file=sys.stderr, flush=True)
+
+    nbytes = algorithmic_bytes(spec, batch.context_lens)
+    achieved = nbytes["total"] / (decode_ms * 1e-3) / 1e9
+    traffic = load_traffic(spec.name)
+    tokens_per_s = batch.num_seqs / (ms_per_step * 1e-3)
+
+    base = None
+    if args.cpu_budget > 0:
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        base = cpu_baseline(batch, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block tables)",
+        "config": {
+            "workload": spec.name, "num_seqs": batch.num_seqs, "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads, "head_size": spec.head_size,
+            "block_size": spec.block_size, "context_lens": f"uniform [{spec.len_lo}, {spec.len_hi}]"
+            if spec.lengths == "uniform" else "lognormal", "num_blocks": batch.num_blocks,
+            "max_context_len": maxlen, "partition_size": args.partition_size,
+            "step": "slot mapping + cache write + decode", "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm", "kernel": "pa_decode (events around the call on its stream)",
+            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes["total"],
+            "bytes_per_token_per_kv_head": nbytes["per_token_head"],
+            "decode_ms_mean": decode_ms, "decode_ms_min": float(np.min(dec_ms))},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * pa.h -- paged decode attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The KV cache is split into fixed-size physical blocks ("pages") that a
+ * per-sequence block table maps logical positions onto:
+ *   key_cache, value_cache : [num_blocks, block_size, num_kv_heads, head_size]
+ *   block_tables           : int32 [num_seqs, max_blocks_per_seq]
+ * Position t of sequence s lives in physical block block_tables[s][t / block_size]
+ * at offset t % block_size, i.e. at flat slot
+ *   block_tables[s][t / block_size] * block_size + t % block_size.
+ * Sources: "01. PagedAttention 详解" (vLLM learning book) §3 for the layout
+ * and the block-table figure; "PagedAttention 机制" (cs-knowledge-wiki)
+ * §5.3.4 for the position -> (block, offset) lookup; the book's §10
+ * (how the table reaches the GPU, the 100k-token table) for one packed int32
+ * table tensor per step.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; tensors are
+ *    contiguous, row-major. The library allocates nothing, keeps no pointer
+ *    after returning, and never synchronises the device.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it asynchronously.
+ *  - The arguments are validated on the host first; a negative status means
+ *    nothing was enqueued. PA_ERR_HIP reports a failed launch.
+ *  - dtype selects the 2-byte storage type shared by q, k, v, both caches and
+ *    out: PA_DTYPE_FP16 (IEEE binary16) or PA_DTYPE_BF16 (bfloat16).
+ *  - Arithmetic is fp32 (products, softmax statistics, accumulation); the
+ *    output is rounded to the storage type with round-to-nearest-even.
+ *  - Concurrent calls on different streams are safe when their outputs and
+ *    workspaces do not overlap.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+enum pa_dtype { PA_DTYPE_FP16 = 0, PA_DTYPE_BF16 = 1 };
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  PA_ERR_SHAPE = -2,       /* sizes inconsistent, negative or out of range       */
+  PA_ERR_DTYPE = -3,       /* unknown dtype code                                  */
+  PA_ERR_UNSUPPORTED = -4, /* valid, but no kernel built for this head size,
+                              block size, group size or partition size            */
+  PA_ERR_WORKSPACE = -5,   /* split-K workspace missing or too small              */
+  PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed          */
+};
+
+/* Supported shapes: head_size in {64, 128}; block_size in {16, 32};
+   num_q_heads / num_kv_heads in {1, 2, 4, 8}. */
+
+/* Library ABI version (PA_ABI_VERSION of the build). */
+PA_API int pa_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+PA_API const char* pa_status_string(int status);
+
+/*
+ * pa_decode_slot_mapping -- slot of each sequence's newest token.
+ *
+ * In a decode step the new token's k/v are appended at the next free slot of
+ * the sequence's last block and then attended to ("01. PagedAttention 详解"
+ * §4, decode phase). With context length L (counting the new token) that is
+ * position L-1:
+ *   slot_mapping[s] = block_tables[s][(L-1) / block_size] * block_size
+ *                     + (L-1) % block_size,           L = context_lens[s];
+ *   slot_mapping[s] = -1 when L <= 0.
+ * block_tables  : int32 [num_seqs, max_blocks_per_seq] (device)
+ * context_lens  : int32 [num_seqs] (device)
+ * slot_mapping  : int32 [num_seqs] (device, written)
+ * A length above max_blocks_per_seq * block_size also yields -1 (the table
+ * row cannot address it). Exact integer arithmetic.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_seqs < 0, max_blocks_per_seq < 1,
+ * block_size < 1).
+ * num_seqs == 0 enqueues nothing and returns PA_OK.
+ */
+PA_API int pa_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t block_size, int32_t* slot_mapping, void* stream);
+
+/*
+ * pa_cache_write -- store new tokens' k/v rows into their cache slots.
+ *
+ * For each token i with 0 <= slot_mapping[i] < num_blocks * block_size:
+ *   key_cache  [slot / block_size, slot % block_size, :, :] = k[i, :, :]
+ *   value_cache[slot / block_size, slot % block_size, :, :] = v[i, :, :]
+ * (the append step of the book's §4 decode phase; the slot formula of its §3
+ * block table). A bit-exact copy. Tokens whose slot is negative or out of
+ * range are skipped (no write). Slots of one call must be distinct; with
+ * duplicates the surviving row is unspecified.
+ * k, v          : [num_tokens, num_kv_heads, head_size] (device)
+ * key_cache,
+ * value_cache   : [num_blocks, block_size, num_kv_heads, head_size] (device, updated)
+ * slot_mapping  : int32 [num_tokens] (device)
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, num_blocks * block_size
+ * beyond INT32_MAX), PA_ERR_DTYPE, PA_ERR_UNSUPPORTED (head_size not a
+ * multiple of 8, or a k / v / cache pointer not 16-byte aligned).
+ * num_tokens == 0 enqueues nothing and returns PA_OK.
+ */
+PA_API int pa_cache_write(const void* k, const void* v, void* key_cache, void* value_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                          int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                          int32_t dtype, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs.
+ *
+ * partition_size < 0 (single pass) needs none (returns 0). partition_size > 0
+ * needs room for the fp32 partials of ceil(max_context_len / partition_size)
+ * partitions per (sequence, query head). partition_size == 0 (automatic)
+ * returns the most any automatic choice can use. Pure host arithmetic.
+ * Returns 0 for invalid (negative) sizes.
+ */
+PA_API size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_size,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode -- one decode step of paged attention.
+ *
+ * For each sequence s with L = context_lens[s] and each query head h:
+ *   g      = h / (num_q_heads / num_kv_heads)          (its kv head)
+ *   K_t, V_t = key_cache / value_cache rows of kv head g at position t,
+ *              reached through block_tables[s] (see the top of this file)
+ *   out[s, h, :] = sum_{t<L} softmax_t(scale * q[s,h,:] . K_t) * V_t
+ * and out[s, h, :] = 0 when L == 0 (the conceptual kernel of
+ * "PagedAttention 机制" §5.3.4 starts from zeros and scales q.k by
+ * 1/sqrt(head_dim); the softmax normalisation is the standard attention of
+ * the book's §4). Only table entries 0 .. ceil(L / block_size) - 1 are read;
+ * cache slots at positions >= L are never used, whatever they hold.
+ *
+ * Long contexts are split into partitions (the book's §4 and §9 name a v2
+ * kernel that splits long sequences this way): each partition keeps its running max, exp-sum and weighted sum of
+ * V in fp32 in the workspace, and a reduce rescales and combines them.
+ *   partition_size < 0 : single pass, one work-group per (sequence, kv head);
+ *   partition_size > 0 : split into partitions of that many tokens
+ *                        (a multiple of 16 and of block_size);
+ *   partition_size == 0: chosen from max_context_len, num_seqs * num_kv_heads
+ *                        and the device's compute-unit count.
+ * q    : [num_seqs, num_q_heads, head_size] (device)
+ * out  : [num_seqs, num_q_heads, head_size] (device, written), dtype of q
+ * context_lens : int32 [num_seqs] (device); each must be <= max_context_len
+ *                and <= max_blocks_per_seq * block_size (larger values are
+ *                clamped to those bounds).
+ * max_context_len : host-known upper bound of the lengths (the scheduler owns
+ *                the lengths on the host); sizes the split.
+ * Table entries that are read must lie in [0, num_blocks); a block id outside
+ * that range is skipped (its tokens contribute nothing) rather than read.
+ * workspace : device buffer, 256-byte aligned, of at least
+ *             pa_decode_workspace_size(...) bytes for the same sizes and
+ *             partition_size (may be NULL when that size is 0). Its contents
+ *             need no initialisation; it is scratch for this call only.
+ * Errors: PA_ERR_DTYPE; PA_ERR_SHAPE (non-positive head counts or sizes,
+ * num_q_heads not a multiple of num_kv_heads, max_context_len above
+ * max_blocks_per_seq * block_size, non-finite scale); PA_ERR_UNSUPPORTED
+ * (head_size, block_size, group size or partition_size outside the built
+ * set; q / cache / out pointers not 16-byte aligned); PA_ERR_NULL;
+ * PA_ERR_WORKSPACE; PA_ERR_HIP. num_seqs == 0 returns PA_OK.
+ */
+PA_API int pa_decode(const void* q, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                     void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_size, int32_t block_size, int64_t num_blocks,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                     int32_t dtype, void* workspace, size_t workspace_size, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,202 @@
+// C-ABI entry points declared in include/pa.h: host-side validation, the
+// single-pass / split-K choice, workspace carving, and launches on the
+// caller's stream. No device memory is allocated and nothing synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kAutoPartition = 512;     // tokens per partition when the split is automatic
+constexpr int kAutoMinPartition = 256;  // smallest partition an automatic choice may use
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, cached per device id.
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ilog2_exact(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return (1 << r) == x ? r : -1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SplitLayout {
+  size_t m_off, l_off, o_off, total;
+};
+
+SplitLayout split_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_size, int64_t parts) {
+  SplitLayout s;
+  const size_t n = (size_t)(num_seqs * num_q_heads * parts);
+  s.m_off = 0;
+  s.l_off = align256(n * sizeof(float));
+  s.o_off = s.l_off + align256(n * sizeof(float));
+  s.total = s.o_off + align256(n * (size_t)head_size * sizeof(float));
+  return s;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The automatic variant choice. Single pass when the batch alone gives every
+// compute unit several work-groups and sequences are short enough that the
+// longest one does not leave the chip idle; otherwise split-K.
+int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  const int cus = device_cu_count();
+  const int64_t items = (int64_t)num_seqs * num_kv_heads;
+  if (max_context_len <= kAutoPartition) return -1;
+  if (cus > 0 && items >= 8LL * cus && max_context_len <= 2 * kAutoPartition) return -1;
+  return kAutoPartition;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes are inconsistent, negative or out of range";
+    case PA_ERR_DTYPE: return "unknown dtype code";
+    case PA_ERR_UNSUPPORTED: return "no kernel for this head size, block size, group size, "
+                                    "partition size or pointer alignment";
+    case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t* slot_mapping, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 1) return PA_ERR_SHAPE;
+  if (block_size < 1) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens || !slot_mapping) return PA_ERR_NULL;
+  const hipError_t e = pa::launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens,
+                                               num_seqs, block_size, slot_mapping,
+                                               (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_cache_write(const void* k, const void* v, void* key_cache, void* value_cache,
+                   const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                   int32_t block_size, int32_t num_kv_heads, int32_t head_size, int32_t dtype,
+                   void* stream) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 0 || block_size < 1 || num_kv_heads < 1 || head_size < 1)
+    return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if ((int64_t)num_kv_heads * head_size > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (head_size % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_UNSUPPORTED;
+  const hipError_t e = pa::launch_cache_write(
+      (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)key_cache, (uint16_t*)value_cache,
+      slot_mapping, num_tokens, num_blocks * (int64_t)block_size, num_kv_heads * head_size,
+      (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_size,
+                                int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 0 || head_size < 0 || max_context_len < 0) return 0;
+  if (partition_size < 0) return 0;
+  const int64_t P = partition_size == 0 ? kAutoMinPartition : partition_size;
+  const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  return split_layout(num_seqs, num_q_heads, head_size, parts).total;
+}
+
+int pa_decode(const void* q, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+              int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+              int32_t max_context_len, int32_t partition_size, int32_t dtype, void* workspace,
+              size_t workspace_size, void* stream) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+
+  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len)
+                                    : partition_size;
+  const bool split = P > 0;
+
+  pa::DecodeParams a;
+  a.q = (const uint16_t*)q;
+  a.kc = (const uint16_t*)key_cache;
+  a.vc = (const uint16_t*)value_cache;
+  a.bt = block_tables;
+  a.lens = context_lens;
+  a.out = (uint16_t*)out;
+  a.ws_m = a.ws_l = a.ws_o = nullptr;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.log2_block_size = ilog2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.len_cap = max_context_len;
+  if (split) {
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+    const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, parts);
+    if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
+    char* ws = (char*)workspace;
+    a.ws_m = (float*)(ws + lay.m_off);
+    a.ws_l = (float*)(ws + lay.l_off);
+    a.ws_o = (float*)(ws + lay.o_off);
+    a.part_tokens = P;
+    a.num_parts = (int32_t)parts;
+  } else {
+    a.part_tokens = max_context_len > 0 ? max_context_len : 1;
+    a.num_parts = 1;
+  }
+  const hipError_t e =
+      pa::launch_decode(a, dtype, head_size, group, split, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

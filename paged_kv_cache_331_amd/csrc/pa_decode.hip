@@ -1,0 +1,380 @@
+// Paged decode attention kernels for gfx950 (CDNA4, wave64).
+//
+// What is computed: for a sequence s and query head h, softmax over the
+// logits scale * q . K_t of positions t < L, then the weighted sum of V_t,
+// with K_t / V_t reached through the sequence's block table
+// ("PagedAttention 机制" §5.3.4 conceptual kernel; "01. PagedAttention 详解"
+// §3 layout and §4 decode loop over the table's blocks). Long sequences are
+// split into partitions whose partial results are combined by a second
+// kernel (the book's §4 / §9: v2 uses split-K over long sequences).
+//
+// Work decomposition (a design for this chip, not taken from the pages):
+//  * One work-group (4 waves) per (kv head g, partition p, sequence s). The G
+//    query heads that share kv head g are all served by that work-group, so
+//    every K/V row is fetched from HBM once per step.
+//  * The partition's block-table entries are staged once into LDS; each wave
+//    reads the block id of its tile from LDS and makes it wave-uniform.
+//  * A wave walks 16-token tiles. Lanes form 8 "token rows" of 8 lanes; a
+//    lane holds 8 (head_size 64) or 16 (head_size 128) dimensions of one
+//    token, so one 16-byte load per lane and vector covers a full 128-byte
+//    line of 8 consecutive slots. The q.k partials are summed inside the
+//    8-lane row with three DPP steps; nothing crosses rows in the loop.
+//  * Each token row keeps its own running max / exp-sum / V accumulator
+//    (online softmax, exact rescaling by exp2(m_old - m_new)); rows, then
+//    waves, are merged once at the end.
+//  * Positions >= L inside the last tile are excluded by select: the logit
+//    becomes -inf and the V row is replaced by zeros, so whatever those slots
+//    hold (even NaN) cannot reach the result. Table entries past the last
+//    block are never read.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+constexpr float kEmptyMax = -1.0e30f;  // running max before any token: finite, so
+                                       // exp2(m_old - m_new) never sees inf - inf
+constexpr int kLanesPerRow = 8;
+constexpr int kRows = 64 / kLanesPerRow;   // token rows per wave instruction
+constexpr int kTile = 16;                  // tokens per wave iteration
+constexpr int kTileGroups = kTile / kRows; // row groups per tile
+constexpr int kTableChunk = 256;           // table entries staged per LDS pass
+
+union Vec16 {
+  uint4 v;
+  uint32_t w[4];
+};
+
+template <class DT, int D, int G, bool SPLIT>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
+  using S = Storage<DT>;
+  constexpr int NW = kDecodeWaves;
+  constexpr int VPR = D / 64;          // 16-byte vectors per lane per token
+  constexpr int DL = VPR * 8;          // dimensions held per lane
+  static_assert(D == 64 || D == 128, "head size");
+
+  __shared__ int32_t s_tbl[kTableChunk];
+  __shared__ float s_part[NW][G][D + 2];
+
+  const int Hkv = a.num_kv_heads;
+  int wg = blockIdx.x;
+  const int g = wg % Hkv;
+  wg /= Hkv;
+  const int p = wg % a.num_parts;
+  const int s = wg / a.num_parts;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int start = p * a.part_tokens;
+  const int tid = threadIdx.x;
+  if (start >= L) {
+    if (!SPLIT && p == 0) {  // empty sequence: the output stays zero
+      uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
+      for (int i = tid; i < G * D; i += NW * 64) o[i] = 0;
+    }
+    return;
+  }
+  const int end = min(L, start + a.part_tokens);
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int row = lane / kLanesPerRow;
+  const int col = lane % kLanesPerRow;
+  const int64_t tok_stride = (int64_t)Hkv * D;        // elements between slots
+  const int64_t lane_elem = row * tok_stride + (int64_t)g * D + col * 8;
+
+  // q slices of the G query heads of this kv head (raw storage words).
+  uint32_t qw[G][VPR][4];
+  {
+    const uint16_t* qs = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D + col * 8;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int v = 0; v < VPR; ++v) {
+        Vec16 t;
+        t.v = *reinterpret_cast<const uint4*>(qs + h * D + v * 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qw[h][v][e] = t.w[e];
+      }
+  }
+
+  float m[G], l[G], acc[G][DL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kEmptyMax;
+    l[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) acc[h][d] = 0.f;
+  }
+
+  const int32_t* bt_row = a.bt + (int64_t)s * a.max_blocks_per_seq;
+  const int bs = a.block_size;
+  const int lbs = a.log2_block_size;
+  const int first_blk = start >> lbs;            // start is block aligned
+  const int end_blk = ((end - 1) >> lbs) + 1;    // one past the last block read
+  const float sl2 = a.scale_log2;
+
+  for (int cb = first_blk; cb < end_blk; cb += kTableChunk) {
+    const int nb = min(kTableChunk, end_blk - cb);
+    if (cb != first_blk) __syncthreads();        // previous chunk fully consumed
+    for (int i = tid; i < nb; i += NW * 64) s_tbl[i] = bt_row[cb + i];
+    __syncthreads();
+    const int t0 = cb << lbs;
+    const int t1 = min(end, (cb + nb) << lbs);
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+
+    for (int it = wave; it < ntiles; it += NW) {
+      const int ts = t0 + it * kTile;            // first position of the tile
+      const int blk = __builtin_amdgcn_readfirstlane(s_tbl[(ts >> lbs) - cb]);
+      if ((uint64_t)(uint32_t)blk >= (uint64_t)a.num_blocks) continue;  // corrupt entry: skip
+      const int off0 = ts & (bs - 1);            // tile never straddles a block (bs % 16 == 0)
+      const int64_t base = ((int64_t)blk * bs + off0) * tok_stride + lane_elem;
+
+      Vec16 kr[kTileGroups][VPR], vr[kTileGroups][VPR];
+#pragma unroll
+      for (int tg = 0; tg < kTileGroups; ++tg)
+#pragma unroll
+        for (int v = 0; v < VPR; ++v)
+          kr[tg][v].v = *reinterpret_cast<const uint4*>(a.kc + base + tg * kRows * tok_stride + v * 64);
+#pragma unroll
+      for (int tg = 0; tg < kTileGroups; ++tg)
+#pragma unroll
+        for (int v = 0; v < VPR; ++v)
+          vr[tg][v].v = *reinterpret_cast<const uint4*>(a.vc + base + tg * kRows * tok_stride + v * 64);
+
+      float lg[G][kTileGroups];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int tg = 0; tg < kTileGroups; ++tg) {
+          float d = 0.f;
+#pragma unroll
+          for (int v = 0; v < VPR; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d = S::dot2(qw[h][v][e], kr[tg][v].w[e], d);
+          lg[h][tg] = row8_sum(d) * sl2;
+        }
+
+      if (ts + kTile > end) {                    // tail tile: mask positions >= end
+#pragma unroll
+        for (int tg = 0; tg < kTileGroups; ++tg) {
+          const bool ok = ts + tg * kRows + row < end;
+#pragma unroll
+          for (int h = 0; h < G; ++h) lg[h][tg] = ok ? lg[h][tg] : -INFINITY;
+#pragma unroll
+          for (int v = 0; v < VPR; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[tg][v].w[e] = ok ? vr[tg][v].w[e] : 0u;
+        }
+      }
+
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = lg[h][0];
+#pragma unroll
+        for (int tg = 1; tg < kTileGroups; ++tg) mx = fmaxf(mx, lg[h][tg]);
+        const float mn = fmaxf(m[h], mx);
+        const float alpha = fast_exp2(m[h] - mn);
+        float pr[kTileGroups];
+        float ps = 0.f;
+#pragma unroll
+        for (int tg = 0; tg < kTileGroups; ++tg) {
+          pr[tg] = fast_exp2(lg[h][tg] - mn);
+          ps += pr[tg];
+        }
+        l[h] = fmaf(l[h], alpha, ps);
+        m[h] = mn;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) acc[h][d] *= alpha;
+#pragma unroll
+        for (int tg = 0; tg < kTileGroups; ++tg)
+#pragma unroll
+          for (int v = 0; v < VPR; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[h][v * 8 + 2 * e] = fmaf(pr[tg], S::lo(vr[tg][v].w[e]), acc[h][v * 8 + 2 * e]);
+              acc[h][v * 8 + 2 * e + 1] = fmaf(pr[tg], S::hi(vr[tg][v].w[e]), acc[h][v * 8 + 2 * e + 1]);
+            }
+      }
+    }
+  }
+
+  // Merge the 8 token rows of each wave (lanes with equal col hold equal dims).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = m[h];
+    M = fmaxf(M, __shfl_xor(M, 8));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float c = fast_exp2(m[h] - M);
+    float lw = l[h] * c;
+    lw += __shfl_xor(lw, 8);
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+#pragma unroll
+    for (int d = 0; d < DL; ++d) {
+      float x = acc[h][d] * c;
+      x += __shfl_xor(x, 8);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[h][d] = x;
+    }
+    m[h] = M;
+    l[h] = lw;
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int v = 0; v < VPR; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_part[wave][h][v * 64 + col * 8 + e] = acc[h][v * 8 + e];
+      if (col == 0) {
+        s_part[wave][h][D] = m[h];
+        s_part[wave][h][D + 1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves: rescale each wave's partial sums to the common max.
+  for (int i = tid; i < G * D; i += NW * 64) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = s_part[0][h][D];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_part[w][h][D]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = fast_exp2(s_part[w][h][D] - M);
+      num = fmaf(c, s_part[w][h][d], num);
+      den = fmaf(c, s_part[w][h][D + 1], den);
+    }
+    const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
+    if (!SPLIT) {
+      a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
+    } else {
+      const int64_t pi = oh * a.num_parts + p;
+      a.ws_o[pi * D + d] = num;
+      if (d == 0) {
+        a.ws_m[pi] = M;
+        a.ws_l[pi] = den;
+      }
+    }
+  }
+}
+
+// Split-K combine: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with
+// M = max_p m_p, over the partitions that hold tokens of the sequence.
+template <class DT, int D>
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams a) {
+  using S = Storage<DT>;
+  constexpr int NW = kReduceThreads / 64;
+  constexpr int DPL = D / 64;           // dimensions per lane
+  __shared__ float s_max[NW];
+  __shared__ float s_acc[NW][D + 1];
+
+  const int h = blockIdx.x % a.num_q_heads;
+  const int s = blockIdx.x / a.num_q_heads;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int64_t oh = (int64_t)s * a.num_q_heads + h;
+  uint16_t* outp = a.out + oh * D;
+  if (L == 0) {
+    for (int d = tid; d < D; d += kReduceThreads) outp[d] = 0;
+    return;
+  }
+  const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  const float* pm = a.ws_m + oh * a.num_parts;
+  const float* pl = a.ws_l + oh * a.num_parts;
+  const float* po = a.ws_o + oh * a.num_parts * D;
+
+  float M = kEmptyMax;
+  for (int i = tid; i < np; i += kReduceThreads) M = fmaxf(M, pm[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = s_max[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_max[w]);
+
+  float num[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) num[e] = 0.f;
+  float den = 0.f;
+  for (int i = wave; i < np; i += NW) {
+    const float c = fast_exp2(pm[i] - M);
+    den = fmaf(c, pl[i], den);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) num[e] = fmaf(c, po[(int64_t)i * D + lane * DPL + e], num[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) s_acc[wave][lane * DPL + e] = num[e];
+  if (lane == 0) s_acc[wave][D] = den;
+  __syncthreads();
+  for (int d = tid; d < D; d += kReduceThreads) {
+    float n = 0.f, dd = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      n += s_acc[w][d];
+      dd += s_acc[w][D];
+    }
+    outp[d] = S::from_float(n / dd);
+  }
+}
+
+template <class DT, int D, int G>
+hipError_t launch_dg(const DecodeParams& a, bool split, hipStream_t st) {
+  const uint64_t nwg = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
+  if (nwg == 0) return hipSuccess;
+  if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
+  if (split) {
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, true>), dim3((uint32_t)nwg),
+                       dim3(kDecodeWaves * 64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint64_t nr = (uint64_t)a.num_q_heads * a.num_seqs;
+    hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), dim3((uint32_t)nr), dim3(kReduceThreads), 0,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, false>), dim3((uint32_t)nwg),
+                       dim3(kDecodeWaves * 64), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <class DT, int D>
+hipError_t launch_d(const DecodeParams& a, int group, bool split, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_dg<DT, D, 1>(a, split, st);
+    case 2: return launch_dg<DT, D, 2>(a, split, st);
+    case 4: return launch_dg<DT, D, 4>(a, split, st);
+    case 8: return launch_dg<DT, D, 8>(a, split, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class DT>
+hipError_t launch_t(const DecodeParams& a, int head_size, int group, bool split, hipStream_t st) {
+  switch (head_size) {
+    case 64: return launch_d<DT, 64>(a, group, split, st);
+    case 128: return launch_d<DT, 128>(a, group, split, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group, bool split,
+                         hipStream_t stream) {
+  return dtype == 0 ? launch_t<Fp16>(a, head_size, group, split, stream)
+                    : launch_t<Bf16>(a, head_size, group, split, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,50 @@
+// Internal launch interface between the C-ABI layer (pa_api.hip) and the
+// kernel translation units. Host-side only; nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one decode launch needs. Pointers are device pointers.
+struct DecodeParams {
+  const uint16_t* q;        // [B, Hq, D]
+  const uint16_t* kc;       // [NB, bs, Hkv, D]
+  const uint16_t* vc;       // [NB, bs, Hkv, D]
+  const int32_t* bt;        // [B, MB]
+  const int32_t* lens;      // [B]
+  uint16_t* out;            // [B, Hq, D]
+  float* ws_m;              // split-K partials: running max (log2 units) [B, Hq, P]
+  float* ws_l;              //                   exp-sum                  [B, Hq, P]
+  float* ws_o;              //                   weighted V sum           [B, Hq, P, D]
+  float scale_log2;         // scale * log2(e): logits are kept in base-2 units
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t part_tokens;      // tokens per partition (multiple of 16 and of block_size)
+  int32_t num_parts;        // partitions per sequence in the grid
+  int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
+};
+
+// Work-groups of the partition kernel per launch: one per
+// (kv head, partition, sequence). Launch shapes are fixed per instantiation.
+constexpr int kDecodeWaves = 4;
+constexpr int kReduceThreads = 256;
+
+hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group,
+                         bool split, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq,
+                               const int32_t* lens, int32_t num_seqs, int32_t block_size,
+                               int32_t* slots, hipStream_t stream);
+
+hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, uint16_t* kc, uint16_t* vc,
+                              const int32_t* slots, int32_t num_tokens, int64_t num_slots,
+                              int32_t row_elems, hipStream_t stream);
+
+}  // namespace pa

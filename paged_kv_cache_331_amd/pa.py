@@ -1,0 +1,157 @@
+"""ctypes binding of the C-ABI HIP library (``include/pa.h``).
+
+Argument marshalling only: tensors become device pointers and sizes, the
+current torch stream becomes the ``hipStream_t``, and a non-zero status
+becomes :class:`PagedAttentionError`. Every step of the computation runs in
+the HIP kernels; there is no fallback. If the built library is missing,
+loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa_gfx950.so")
+
+PA_DTYPE_FP16 = 0
+PA_DTYPE_BF16 = 1
+PA_OK = 0
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
+          -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP"}
+
+_i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_void_p, ctypes.c_size_t)
+
+# name -> (restype, argtypes); mirrors include/pa.h
+SIGNATURES = {
+    "pa_abi_version": (ctypes.c_int, []),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_decode_slot_mapping": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _vp, _vp]),
+    "pa_cache_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+                                      _i32, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PagedAttentionError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run `python -m paged_kv_cache_331_amd.build`)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load().pa_abi_version())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PagedAttentionError(fn, status)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float16:
+        return PA_DTYPE_FP16
+    if t == torch.bfloat16:
+        return PA_DTYPE_BF16
+    raise TypeError(f"unsupported storage dtype {t}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def decode_slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        block_size: int, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Slot of each sequence's newest token (position L-1), -1 for L == 0."""
+    B, MB = block_tables.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=block_tables.device)
+    st = load().pa_decode_slot_mapping(_dev(block_tables, "block_tables"), MB,
+                                       _dev(context_lens, "context_lens"), B, int(block_size),
+                                       _dev(out, "slot_mapping"), _stream(stream))
+    _check("pa_decode_slot_mapping", st)
+    return out
+
+
+def cache_write(k: torch.Tensor, v: torch.Tensor, key_cache: torch.Tensor,
+                value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Store k[i], v[i] ([T, Hkv, D]) at slot_mapping[i] of the caches, in place."""
+    NB, bs, Hkv, D = key_cache.shape
+    T = k.shape[0]
+    st = load().pa_cache_write(_dev(k, "k"), _dev(v, "v"), _dev(key_cache, "key_cache"),
+                               _dev(value_cache, "value_cache"),
+                               _dev(slot_mapping, "slot_mapping"), T, NB, bs, Hkv, D,
+                               dtype_code(key_cache.dtype), _stream(stream))
+    _check("pa_cache_write", st)
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_size: int,
+                          max_context_len: int, partition_size: int = 0) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, head_size,
+                                               max_context_len, partition_size))
+
+
+def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           max_context_len: int, out: Optional[torch.Tensor] = None,
+           partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """One paged decode-attention step; returns ``out`` ([B, Hq, D], dtype of q)."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().pa_decode(_dev(q, "q"), _dev(key_cache, "key_cache"),
+                          _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+                          _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
+                          B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), int(partition_size),
+                          dtype_code(q.dtype), ws_ptr, ws_len, _stream(stream))
+    _check("pa_decode", st)
+    return out

@@ -57,21 +57,34 @@ template <> struct Storage<Bf16> {
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // row_mirror: lane i <-> 15-i within 16 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over the 8 consecutive lanes (one token row) holding slices of one dot
-// product. Butterfly: xor 1, xor 2 inside quads, then the half-row mirror
-// pairs quad 0 with quad 1. Every lane of the row ends with the full sum.
+// Sum over LANES (8 or 16) consecutive lanes -- one token row -- holding
+// slices of one dot product. Butterfly: xor 1 and xor 2 inside quads, the
+// half-row mirror pairs quad 0 with quad 1, the row mirror pairs the two
+// halves of a 16-lane row. Every lane of the row ends with the full sum.
 // All 64 lanes must be active.
-__device__ __forceinline__ float row8_sum(float x) {
+template <int LANES>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(LANES == 8 || LANES == 16, "row width");
   x += dpp<kDppQuadXor1>(x);
   x += dpp<kDppQuadXor2>(x);
   x += dpp<kDppHalfMirror>(x);
+  if (LANES == 16) x += dpp<kDppMirror>(x);
   return x;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: K/V rows are streamed once per step, so
+// they should not displace anything else from the caches.
+__device__ __forceinline__ u32x4_t load_stream16(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -73,7 +73,7 @@ def kernel_source_sha() -> str:
 
 
 def load_traffic(workload: str):
-    """Counter-measured HBM traffic per decode launch, if taken on this kernel source."""
+    """Counter-measured HBM traffic per decode call, if taken on this kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -85,8 +85,71 @@ def load_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
+def _pmc_rows(path: str):
+    import csv
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            yield r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+
+
+def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+               copy_write_csv: str, copy_bytes: int = 1 << 30) -> dict:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE dispatch records into bytes per decode call.
+
+    Each counter is scaled by what it reads for a device copy of
+    ``copy_bytes`` (the calibration run, ``--copy-probe``): the copy fetches
+    and writes exactly ``copy_bytes``. A decode call is the partition kernel
+    plus, when split, the reduce kernel; the median over dispatches of each
+    is summed. The record is keyed to the kernel sources' hash so that it
+    stops being reported once the kernels change.
+    """
+    def median_kib(path, counter, match):
+        vals = [v for k, c, v in _pmc_rows(path) if c == counter and match(k)]
+        if not vals:
+            raise ValueError(f"no {counter} rows for the kernel in {path}")
+        return float(np.median(vals)), len(vals)
+
+    copy_kib = copy_bytes / 1024.0
+    is_copy = lambda k: "copyBuffer" in k
+    cf, _ = median_kib(copy_fetch_csv, "FETCH_SIZE", is_copy)
+    cw, _ = median_kib(copy_write_csv, "WRITE_SIZE", is_copy)
+    f_fetch, f_write = copy_kib / cf, copy_kib / cw
+    rec = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_fetch,
+           "write_scale": f_write, "kernels": {}}
+    total = 0.0
+    for tag in ("decode_partition_kernel", "decode_reduce_kernel"):
+        m = lambda k, tag=tag: tag in k
+        try:
+            fk, n = median_kib(fetch_csv, "FETCH_SIZE", m)
+        except ValueError:
+            continue
+        wk, _ = median_kib(write_csv, "WRITE_SIZE", m)
+        fb, wb = fk * f_fetch * 1024, wk * f_write * 1024
+        rec["kernels"][tag] = {"dispatches": n, "fetch_kib_raw": fk, "write_kib_raw": wk,
+                               "fetch_bytes": fb, "write_bytes": wb}
+        total += fb + wb
+    rec["bytes_per_launch"] = total
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def cpu_baseline(batch, budget_s: float) -> dict:
-    """Time the fp64 oracle (as it stands) on a prefix of the batch's sequences."""
+    """Time the fp64 oracle (as it stands) on a bounded sample of the batch.
+
+    Sequences are taken in order, wrapping round to the first one again,
+    until ``budget_s`` seconds of oracle work have been spent; the rate is
+    decoded tokens (one per sequence visited) per second of single-thread
+    CPU time.
+    """
     import oracle
     try:
         from threadpoolctl import threadpool_limits
@@ -96,7 +159,8 @@ def cpu_baseline(batch, budget_s: float) -> dict:
     done = 0
     t0 = time.perf_counter()
     try:
-        for s in range(batch.num_seqs):
+        while True:
+            s = done % batch.num_seqs
             oracle.slot_mapping(batch.block_tables[s:s + 1], batch.context_lens[s:s + 1],
                                 batch.spec.block_size)
             oracle.decode(batch.q, batch.key_cache, batch.value_cache, batch.block_tables,
@@ -108,10 +172,41 @@ def cpu_baseline(batch, budget_s: float) -> dict:
         if ctx is not None:
             ctx.__exit__(None, None, None)
     dt = time.perf_counter() - t0
+    passes = done / batch.num_seqs
     return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle (slot of the newest token + attention, single "
-                       f"thread) over the first {done} of {batch.num_seqs} sequences of the "
-                       f"same batch, {dt:.1f} s; one decoded token per sequence")}
+            "sample": (f"fp64 NumPy oracle (slot of the newest token + attention over every "
+                       f"cached position), one thread, {done} sequence decodes = {passes:.2f} "
+                       f"passes over the {batch.num_seqs}-sequence batch in {dt:.1f} s; one "
+                       f"decoded token per sequence")}
+
+
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 20) -> dict:
+    """Device-to-device copy of ``nbytes`` (torch ``copy_``), timed with events.
+
+    Reported as (read + write bytes) / time: the practical HBM ceiling the
+    decode kernel is compared with, and the known-size copy that calibrates
+    the FETCH_SIZE / WRITE_SIZE counters.
+    """
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        ms.append((e0, e1))
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ms])) * 1e-3
+    del src, dst
+    return {"bytes": nbytes, "GBs": 2 * nbytes / t / 1e9, "ms": t * 1e3}
 
 
 def main(argv=None) -> int:
@@ -124,7 +219,15 @@ def main(argv=None) -> int:
                     help="0 automatic, <0 single pass, >0 split-K partition tokens")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only time a 1 GiB device copy (the counter calibration run)")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="record the traffic of --workload from rocprofv3 counter_collection "
+                         "CSVs (no GPU needed)")
     args = ap.parse_args(argv)
+    if args.ingest_pmc:
+        print(json.dumps(ingest_pmc(args.workload, *args.ingest_pmc), indent=1))
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
@@ -140,6 +243,9 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        print(json.dumps({"copy_probe": copy_bandwidth()}), flush=True)
+        return 0
     pa.load()          # the HIP library must be built; there is no fallback
     spec = wl.CONFIGS[args.workload]
     print(f"# generating {spec.name}", file=sys.stderr, flush=True)
@@ -191,8 +297,13 @@ def main(argv=None) -> int:
     print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode {decode_ms:.4f} ms",
           file=sys.stderr, flush=True)
 
+    copy = copy_bandwidth()
     nbytes = algorithmic_bytes(spec, batch.context_lens)
-    achieved = nbytes["total"] / (decode_ms * 1e-3) / 1e9
+    # A block shared by many tables must come from HBM at least once, so the
+    # roofline counts the shared prefix once; the per-sequence (logical)
+    # rate is reported beside it.
+    achieved = nbytes["total_unique"] / (decode_ms * 1e-3) / 1e9
+    logical = nbytes["total"] / (decode_ms * 1e-3) / 1e9
     traffic = load_traffic(spec.name)
     tokens_per_s = batch.num_seqs / (ms_per_step * 1e-3)
 
@@ -226,9 +337,12 @@ def main(argv=None) -> int:
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes["total"],
+            "algorithmic_bytes_per_launch": nbytes["total_unique"],
+            "logical_bytes_per_launch": nbytes["total"], "logical_GBs": logical,
             "bytes_per_token_per_kv_head": nbytes["per_token_head"],
-            "decode_ms_mean": decode_ms, "decode_ms_min": float(np.min(dec_ms))},
+            "decode_ms_mean": decode_ms, "decode_ms_median": float(np.median(dec_ms)),
+            "decode_ms_min": float(np.min(dec_ms)),
+            "measured_copy_GBs": copy["GBs"], "frac_of_copy": achieved / copy["GBs"]},
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

@@ -331,6 +331,9 @@ def main(argv=None) -> int:
             "block_size": spec.block_size, "context_lens": f"uniform [{spec.len_lo}, {spec.len_hi}]"
             if spec.lengths == "uniform" else "lognormal", "num_blocks": batch.num_blocks,
             "max_context_len": maxlen, "partition_size": args.partition_size,
+            "partition_tokens_used": (args.partition_size if args.partition_size != 0 else
+                                      pa.decode_partition_size(batch.num_seqs, spec.num_kv_heads,
+                                                               maxlen)),
             "step": "slot mapping + cache write + decode", "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm", "kernel": "pa_decode (events around the call on its stream)",

@@ -129,6 +129,23 @@ PA_API size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, in
                                        int32_t max_context_len, int32_t partition_size);
 
 /*
+ * pa_decode_partition_size -- the split pa_decode makes with partition_size 0.
+ *
+ * Returns the tokens per partition of the automatic choice, or -1 for a
+ * single pass, for a batch of num_seqs sequences with num_kv_heads kv heads
+ * whose longest context is max_context_len. The rule: the largest power of
+ * two in [256, 4096] that still gives about four work-groups per compute
+ * unit; at most 1024 when the (sequence, kv head) pairs alone give that many;
+ * no split when the longest context is at most 1.5 partitions. num_cus <= 0
+ * asks the current HIP device for its compute-unit count (256 if it cannot
+ * be queried). Pure host arithmetic otherwise; no device work is enqueued.
+ * Returns 0 for invalid sizes (num_seqs < 0, num_kv_heads < 1,
+ * max_context_len < 0).
+ */
+PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t max_context_len, int32_t num_cus);
+
+/*
  * pa_decode -- one decode step of paged attention.
  *
  * For each sequence s with L = context_lens[s] and each query head h:
@@ -143,13 +160,16 @@ PA_API size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, in
  * cache slots at positions >= L are never used, whatever they hold.
  *
  * Long contexts are split into partitions (the book's §4 and §9 name a v2
- * kernel that splits long sequences this way): each partition keeps its running max, exp-sum and weighted sum of
- * V in fp32 in the workspace, and a reduce rescales and combines them.
+ * kernel that splits long sequences this way): each partition keeps its
+ * running max, exp-sum and weighted sum of V in fp32 in the workspace, and a
+ * second kernel rescales and combines them for the sequences that span more
+ * than one partition (a sequence with one partition is finished directly).
  *   partition_size < 0 : single pass, one work-group per (sequence, kv head);
  *   partition_size > 0 : split into partitions of that many tokens
  *                        (a multiple of 16 and of block_size);
  *   partition_size == 0: chosen from max_context_len, num_seqs * num_kv_heads
- *                        and the device's compute-unit count.
+ *                        and the device's compute-unit count
+ *                        (pa_decode_partition_size).
  * q    : [num_seqs, num_q_heads, head_size] (device)
  * out  : [num_seqs, num_q_heads, head_size] (device, written), dtype of q
  * context_lens : int32 [num_seqs] (device); each must be <= max_context_len

@@ -11,8 +11,10 @@
 
 namespace {
 
-constexpr int kAutoPartition = 512;     // tokens per partition when the split is automatic
-constexpr int kAutoMinPartition = 256;  // smallest partition an automatic choice may use
+constexpr int kAutoMinPartition = 256;       // partition sizes an automatic choice may use
+constexpr int kAutoMaxPartition = 4096;
+constexpr int kAutoBalancedPartition = 1024;  // cap when the batch alone fills the chip
+constexpr int kFallbackCUs = 256;             // if the device cannot be queried
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -58,15 +60,26 @@ SplitLayout split_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_siz
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The automatic variant choice. Single pass when the batch alone gives every
-// compute unit several work-groups and sequences are short enough that the
-// longest one does not leave the chip idle; otherwise split-K.
-int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  const int cus = device_cu_count();
+// The automatic partition size (tokens), or -1 for a single pass. The
+// largest power of two in [256, 4096] that still yields about four
+// work-groups per compute unit; once the (sequence, kv head) pairs alone give
+// that many, partitions only trim the tail left by the longest sequences and
+// are held at 1024 tokens. A split that would cut no more than a short tail
+// off the longest sequence is not worth its combine. The thresholds come
+// from a sweep of 128..4096-token partitions over the decode workloads.
+int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int cus) {
   const int64_t items = (int64_t)num_seqs * num_kv_heads;
-  if (max_context_len <= kAutoPartition) return -1;
-  if (cus > 0 && items >= 8LL * cus && max_context_len <= 2 * kAutoPartition) return -1;
-  return kAutoPartition;
+  const int64_t target = 4LL * cus;
+  int P = kAutoMinPartition;
+  for (int c = kAutoMaxPartition; c >= kAutoMinPartition; c /= 2) {
+    if (items * ceil_div(max_context_len, c) >= target) {
+      P = c;
+      break;
+    }
+  }
+  if (items >= target && P > kAutoBalancedPartition) P = kAutoBalancedPartition;
+  if (2LL * max_context_len <= 3LL * P) return -1;
+  return P;
 }
 
 }  // namespace
@@ -123,6 +136,14 @@ int pa_cache_write(const void* k, const void* v, void* key_cache, void* value_ca
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t num_cus) {
+  if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0) return 0;
+  int cus = num_cus > 0 ? num_cus : device_cu_count();
+  if (cus <= 0) cus = kFallbackCUs;
+  return auto_partition(num_seqs, num_kv_heads, max_context_len, cus);
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_size,
                                 int32_t max_context_len, int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads < 0 || head_size < 0 || max_context_len < 0) return 0;
@@ -158,7 +179,9 @@ int pa_decode(const void* q, const void* key_cache, const void* value_cache,
   if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
     return PA_ERR_UNSUPPORTED;
 
-  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len)
+  int cus = device_cu_count();
+  if (cus <= 0) cus = kFallbackCUs;
+  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, cus)
                                     : partition_size;
   const bool split = P > 0;
 
@@ -190,12 +213,15 @@ int pa_decode(const void* q, const void* key_cache, const void* value_cache,
     a.ws_o = (float*)(ws + lay.o_off);
     a.part_tokens = P;
     a.num_parts = (int32_t)parts;
+    // Few (sequence, kv head) pairs: order the grid sequence by sequence.
+    a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
   } else {
     a.part_tokens = max_context_len > 0 ? max_context_len : 1;
     a.num_parts = 1;
+    a.seq_major = 0;
   }
   const hipError_t e =
-      pa::launch_decode(a, dtype, head_size, group, split, (hipStream_t)stream);
+      pa::launch_decode(a, dtype, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

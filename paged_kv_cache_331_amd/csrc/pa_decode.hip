@@ -5,8 +5,8 @@
 // with K_t / V_t reached through the sequence's block table
 // ("PagedAttention 机制" §5.3.4 conceptual kernel; "01. PagedAttention 详解"
 // §3 layout and §4 decode loop over the table's blocks). Long sequences are
-// split into partitions whose partial results are combined by a second
-// kernel (the book's §4 / §9: v2 uses split-K over long sequences).
+// split into partitions (the book's §4 / §9: v2 uses split-K over long
+// sequences) whose partial results a second kernel combines.
 //
 // Work decomposition (a design for this chip, not taken from the pages):
 //  * One work-group (4 waves) per (kv head g, partition p, sequence s). The G
@@ -44,7 +44,7 @@ union Vec16 {
   uint32_t w[4];
 };
 
-template <class DT, int D, int G, bool SPLIT>
+template <class DT, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   using S = Storage<DT>;
   constexpr int NW = kDecodeWaves;
@@ -52,26 +52,33 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   constexpr int ROWS = 64 / LPR;       // token rows per load instruction
   constexpr int TG = kTile / ROWS;     // load instructions per tile and tensor
   constexpr int DL = 8;                // dimensions held per lane
+  constexpr int NT = NW * 64;
   static_assert(D == 64 || D == 128, "head size");
 
   __shared__ int32_t s_tbl[kTableChunk];
   __shared__ float s_part[NW][G][D + 2];
 
+  // Work-groups are numbered kv head fastest. With many (sequence, kv head)
+  // pairs the partition index comes last: every sequence's first partition
+  // is dispatched before any second one, and partitions past a sequence's
+  // end (which exit at once) gather at the end of the grid. With few pairs
+  // (long contexts) the sequence index comes last, so one sequence's
+  // partitions run together; each order measured faster in its regime.
   const int Hkv = a.num_kv_heads;
   int wg = blockIdx.x;
   const int g = wg % Hkv;
   wg /= Hkv;
-  const int p = wg % a.num_parts;
-  const int s = wg / a.num_parts;
+  const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
+  const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
 
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int start = p * a.part_tokens;
   const int tid = threadIdx.x;
   if (start >= L) {
-    if (!SPLIT && p == 0) {  // empty sequence: the output stays zero
+    if (p == 0) {  // empty sequence: the output stays zero
       uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
-      for (int i = tid; i < G * D; i += NW * 64) o[i] = 0;
+      for (int i = tid; i < G * D; i += NT) o[i] = 0;
     }
     return;
   }
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   for (int cb = first_blk; cb < end_blk; cb += kTableChunk) {
     const int nb = min(kTableChunk, end_blk - cb);
     if (cb != first_blk) __syncthreads();        // previous chunk fully consumed
-    for (int i = tid; i < nb; i += NW * 64) s_tbl[i] = bt_row[cb + i];
+    for (int i = tid; i < nb; i += NT) s_tbl[i] = bt_row[cb + i];
     __syncthreads();
     const int t0 = cb << lbs;
     const int t1 = min(end, (cb + nb) << lbs);
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   __syncthreads();
 
   // Merge the waves: rescale each wave's partial sums to the common max.
-  for (int i = tid; i < G * D; i += NW * 64) {
+  const int np = (L + a.part_tokens - 1) / a.part_tokens;  // partitions holding tokens
+  for (int i = tid; i < G * D; i += NT) {
     const int h = i / D;
     const int d = i % D;
     float M = s_part[0][h][D];
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
       den = fmaf(c, s_part[w][h][D + 1], den);
     }
     const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
-    if (!SPLIT) {
+    if (np == 1) {
       a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
     } else {
       const int64_t pi = oh * a.num_parts + p;
@@ -247,116 +255,124 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   }
 }
 
-// Split-K combine: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with
-// M = max_p m_p, over the partitions that hold tokens of the sequence.
+// Split-K combine for the sequences with two or more partitions:
+//   out = sum_q 2^(m_q - M) o_q / sum_q 2^(m_q - M) l_q,   M = max_q m_q,
+// over the partitions q that hold tokens. One work-group per (sequence,
+// query head). Threads own a 16-byte chunk of the output row and a strided
+// subset of the partitions, so a long sequence's partials are read with
+// every thread's loads in flight at once; the subsets are summed through
+// LDS. Sequences with one partition were finished by the partition kernel.
 template <class DT, int D>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const DecodeParams a) {
   using S = Storage<DT>;
-  constexpr int NW = kReduceThreads / 64;
-  constexpr int DPL = D / 64;           // dimensions per lane
+  constexpr int NT = kReduceThreads;
+  constexpr int NW = NT / 64;
+  constexpr int CH = D / 4;              // 16-byte chunks of one output row
+  constexpr int GROUPS = NT / CH;        // partition subsets
   __shared__ float s_max[NW];
-  __shared__ float s_acc[NW][D + 1];
+  __shared__ float s_sum[NT][5];
 
   const int h = blockIdx.x % a.num_q_heads;
   const int s = blockIdx.x / a.num_q_heads;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int64_t oh = (int64_t)s * a.num_q_heads + h;
-  uint16_t* outp = a.out + oh * D;
-  if (L == 0) {
-    for (int d = tid; d < D; d += kReduceThreads) outp[d] = 0;
-    return;
-  }
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+
+  const int64_t oh = (int64_t)s * a.num_q_heads + h;
   const float* pm = a.ws_m + oh * a.num_parts;
   const float* pl = a.ws_l + oh * a.num_parts;
-  const float* po = a.ws_o + oh * a.num_parts * D;
 
+  // M = max over the partitions' running maxima.
   float M = kEmptyMax;
-  for (int i = tid; i < np; i += kReduceThreads) M = fmaxf(M, pm[i]);
+  for (int q = tid; q < np; q += NT) M = fmaxf(M, pm[q]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) s_max[wave] = M;
+  if ((tid & 63) == 0) s_max[tid >> 6] = M;
   __syncthreads();
   M = s_max[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) M = fmaxf(M, s_max[w]);
 
-  float num[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) num[e] = 0.f;
+  const int c = tid % CH;
+  const int grp = tid / CH;
+  const float4* po = reinterpret_cast<const float4*>(a.ws_o + oh * a.num_parts * D) + c;
   float den = 0.f;
-  for (int i = wave; i < np; i += NW) {
-    const float c = fast_exp2(pm[i] - M);
-    den = fmaf(c, pl[i], den);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) num[e] = fmaf(c, po[(int64_t)i * D + lane * DPL + e], num[e]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int q = grp; q < np; q += GROUPS) {
+    const float w = fast_exp2(pm[q] - M);
+    const float4 o = po[(int64_t)q * CH];
+    den = fmaf(w, pl[q], den);
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
   }
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) s_acc[wave][lane * DPL + e] = num[e];
-  if (lane == 0) s_acc[wave][D] = den;
+  float* r = s_sum[tid];
+  r[0] = den;
+  r[1] = acc.x;
+  r[2] = acc.y;
+  r[3] = acc.z;
+  r[4] = acc.w;
   __syncthreads();
-  for (int d = tid; d < D; d += kReduceThreads) {
-    float n = 0.f, dd = 0.f;
+  if (grp != 0) return;
+  float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      n += s_acc[w][d];
-      dd += s_acc[w][D];
-    }
-    outp[d] = S::from_float(n / dd);
+  for (int k = 0; k < GROUPS; ++k) {
+#pragma unroll
+    for (int e = 0; e < 5; ++e) t[e] += s_sum[k * CH + c][e];
   }
+  const float inv = 1.f / t[0];
+  uint2 packed;
+  packed.x = (uint32_t)S::from_float(t[1] * inv) | ((uint32_t)S::from_float(t[2] * inv) << 16);
+  packed.y = (uint32_t)S::from_float(t[3] * inv) | ((uint32_t)S::from_float(t[4] * inv) << 16);
+  *reinterpret_cast<uint2*>(a.out + oh * D + c * 4) = packed;
 }
 
 template <class DT, int D, int G>
-hipError_t launch_dg(const DecodeParams& a, bool split, hipStream_t st) {
+hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   const uint64_t nwg = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  if (split) {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, true>), dim3((uint32_t)nwg),
-                       dim3(kDecodeWaves * 64), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const uint64_t nr = (uint64_t)a.num_q_heads * a.num_seqs;
-    hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), dim3((uint32_t)nr), dim3(kReduceThreads), 0,
-                       st, a);
-  } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, false>), dim3((uint32_t)nwg),
-                       dim3(kDecodeWaves * 64), 0, st, a);
-  }
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>), dim3((uint32_t)nwg),
+                     dim3(kDecodeWaves * 64), 0, st, a);
+  if (a.num_parts == 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t nr = (uint64_t)a.num_q_heads * a.num_seqs;
+  hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), dim3((uint32_t)nr), dim3(kReduceThreads), 0,
+                     st, a);
   return hipGetLastError();
 }
 
 template <class DT, int D>
-hipError_t launch_d(const DecodeParams& a, int group, bool split, hipStream_t st) {
+hipError_t launch_d(const DecodeParams& a, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_dg<DT, D, 1>(a, split, st);
-    case 2: return launch_dg<DT, D, 2>(a, split, st);
-    case 4: return launch_dg<DT, D, 4>(a, split, st);
-    case 8: return launch_dg<DT, D, 8>(a, split, st);
+    case 1: return launch_dg<DT, D, 1>(a, st);
+    case 2: return launch_dg<DT, D, 2>(a, st);
+    case 4: return launch_dg<DT, D, 4>(a, st);
+    case 8: return launch_dg<DT, D, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class DT>
-hipError_t launch_t(const DecodeParams& a, int head_size, int group, bool split, hipStream_t st) {
+hipError_t launch_t(const DecodeParams& a, int head_size, int group, hipStream_t st) {
   switch (head_size) {
-    case 64: return launch_d<DT, 64>(a, group, split, st);
-    case 128: return launch_d<DT, 128>(a, group, split, st);
+    case 64: return launch_d<DT, 64>(a, group, st);
+    case 128: return launch_d<DT, 128>(a, group, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group, bool split,
+hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group,
                          hipStream_t stream) {
-  return dtype == 0 ? launch_t<Fp16>(a, head_size, group, split, stream)
-                    : launch_t<Bf16>(a, head_size, group, split, stream);
+  return dtype == 0 ? launch_t<Fp16>(a, head_size, group, stream)
+                    : launch_t<Bf16>(a, head_size, group, stream);
 }
 
 }  // namespace pa

@@ -26,8 +26,10 @@ struct DecodeParams {
   int32_t log2_block_size;
   int32_t max_blocks_per_seq;
   int64_t num_blocks;
-  int32_t part_tokens;      // tokens per partition (multiple of 16 and of block_size)
-  int32_t num_parts;        // partitions per sequence in the grid
+  int32_t part_tokens;      // tokens per partition (multiple of 16 and of block_size);
+                            // at least max_context_len when there is no split
+  int32_t num_parts;        // partitions per sequence in the grid (1: no split, no workspace)
+  int32_t seq_major;        // grid order: 1 = sequence index slowest, 0 = partition slowest
   int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
 };
 
@@ -36,8 +38,9 @@ struct DecodeParams {
 constexpr int kDecodeWaves = 4;
 constexpr int kReduceThreads = 256;
 
+// One decode step: the partition kernel, then (num_parts > 1) the combine.
 hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group,
-                         bool split, hipStream_t stream);
+                         hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq,
                                const int32_t* lens, int32_t num_seqs, int32_t block_size,

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_expected_api():
     assert _declared() == sorted(["pa_abi_version", "pa_status_string", "pa_decode_slot_mapping",
-                                  "pa_cache_write", "pa_decode_workspace_size", "pa_decode"])
+                                  "pa_cache_write", "pa_decode_workspace_size",
+                                  "pa_decode_partition_size", "pa_decode"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -141,3 +142,22 @@ def test_cache_write_zero_tokens_ok(lib):
 def test_slot_mapping_validation(lib, args, code):
     bt, mb, lens, n, bs, out = args
     assert pa.load().pa_decode_slot_mapping(bt, mb, lens, n, bs, out, None) == code
+
+
+@pytest.mark.parametrize("B,Hkv,maxlen,cus,expect", [
+    (64, 32, 2046, 256, 1024),     # MHA batch: enough pairs, split held at 1024 tokens
+    (256, 8, 4096, 256, 1024),     # GQA batch with a lognormal length tail
+    (128, 8, 1536, 256, -1),       # longest context within 1.5 partitions: single pass
+    (4, 8, 93064, 256, 2048),      # long contexts: largest split with >= 4 WGs per CU
+    (4, 4, 99, 256, -1),           # tiny batch
+    (1, 8, 8192, 256, 256),        # too few pairs for the target: smallest partition
+    (4, 8, 93064, 64, 4096),       # a smaller device needs fewer work-groups
+    (0, 8, 0, 256, -1),
+])
+def test_auto_partition_rule(lib, B, Hkv, maxlen, cus, expect):
+    assert pa.decode_partition_size(B, Hkv, maxlen, cus) == expect
+
+
+def test_auto_partition_invalid(lib):
+    assert pa.decode_partition_size(-1, 8, 10, 256) == 0
+    assert pa.decode_partition_size(1, 0, 10, 256) == 0

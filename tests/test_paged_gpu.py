@@ -210,3 +210,4 @@ def test_decode_on_side_stream():
         out = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len)
     s.synchronize()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+

@@ -11,4 +11,8 @@ to facts outside itself live in ``tests/test_oracle.py``. No function here is
 "parity unpinned".
 """
 from .paged_attention import *  # noqa: F401,F403
-from .paged_attention import __all__  # noqa: F401
+from .paged_attention import __all__ as _pa_all
+from .fp8 import *  # noqa: F401,F403
+from .fp8 import __all__ as _fp8_all
+
+__all__ = list(_pa_all) + list(_fp8_all)

@@ -34,6 +34,11 @@ What it computes, with the passage each step follows:
 Storage values arrive as uint16 bit patterns with a dtype tag; they are
 upcast exactly to float64. ``scale`` is the float32 value handed to the
 library, upcast. Results are float64 and unrounded.
+
+An FP8 cache (the article's §4.3 FP8 K/V; encoding in :mod:`oracle.fp8`)
+holds uint8 E4M3 codes and one fp32 scale per tensor: a cached row stands for
+``decode(code) * scale``, computed exactly in float64. The query and the
+output keep their 2-byte type.
 """
 from __future__ import annotations
 
@@ -49,7 +54,10 @@ __all__ = [
 
 
 def to_float64(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact upcast of fp16 / bf16 bit patterns to float64."""
+    """Exact upcast of fp16 / bf16 bit patterns (or E4M3 codes) to float64."""
+    if dtype == "fp8":
+        from .fp8 import e4m3_decode
+        return e4m3_decode(bits)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "fp16":
         return bits.view(np.float16).astype(np.float64)
@@ -101,12 +109,16 @@ def cache_write(key_cache: np.ndarray, value_cache: np.ndarray,
 
 
 def gather_positions(cache: np.ndarray, table_row: np.ndarray, length: int,
-                     kv_head: int, dtype: str) -> np.ndarray:
-    """Rows ``cache[table[t // bs], t % bs, kv_head, :]`` for t < length, as float64."""
+                     kv_head: int, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Rows ``cache[table[t // bs], t % bs, kv_head, :]`` for t < length, as float64.
+
+    For an FP8 cache each row is multiplied by the tensor's scale.
+    """
     bs = cache.shape[1]
     t = np.arange(int(length), dtype=np.int64)
     blocks = np.asarray(table_row, dtype=np.int64)[t // bs]
-    return to_float64(cache[blocks, t % bs, kv_head, :], dtype)
+    rows = to_float64(cache[blocks, t % bs, kv_head, :], dtype)
+    return rows * float(np.float32(scale)) if dtype == "fp8" else rows
 
 
 def _softmax_attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray,
@@ -120,16 +132,18 @@ def _softmax_attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 def decode_one(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                block_tables: np.ndarray, context_lens: np.ndarray, scale,
-               dtype: str, seq: int, head: int) -> np.ndarray:
+               dtype: str, seq: int, head: int, cache_dtype: Optional[str] = None,
+               k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Output row ``out[seq, head, :]`` in float64."""
+    cdt = cache_dtype or dtype
     Hq = q.shape[1]
     Hkv = key_cache.shape[2]
     g = head // (Hq // Hkv)
     L = int(context_lens[seq])
     if L == 0:
         return np.zeros(q.shape[2], dtype=np.float64)
-    K = gather_positions(key_cache, block_tables[seq], L, g, dtype)
-    V = gather_positions(value_cache, block_tables[seq], L, g, dtype)
+    K = gather_positions(key_cache, block_tables[seq], L, g, cdt, k_scale)
+    V = gather_positions(value_cache, block_tables[seq], L, g, cdt, v_scale)
     qv = to_float64(q[seq, head], dtype)
     out, _ = _softmax_attend(qv, K, V, float(np.float32(scale)))
     return out
@@ -137,12 +151,18 @@ def decode_one(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
 
 def decode(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
            block_tables: np.ndarray, context_lens: np.ndarray, scale,
-           dtype: str, seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+           dtype: str, seqs: Optional[Iterable[int]] = None,
+           cache_dtype: Optional[str] = None, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> np.ndarray:
     """``out[s, h, :] = softmax(scale * q[s,h] . K_g^T) V_g`` over positions < L_s.
 
     Returns float64 ``[len(seqs), Hq, D]`` (all sequences by default). Each kv
     head's rows are gathered once and reused by its query-head group.
+    ``dtype`` is the query's storage type; ``cache_dtype`` (default: the
+    same) is the caches', and an FP8 cache's rows are scaled by
+    ``k_scale`` / ``v_scale``.
     """
+    cdt = cache_dtype or dtype
     B, Hq, D = q.shape
     Hkv = key_cache.shape[2]
     G = Hq // Hkv
@@ -154,8 +174,8 @@ def decode(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
         if L == 0:
             continue
         for g in range(Hkv):
-            K = gather_positions(key_cache, block_tables[s], L, g, dtype)
-            V = gather_positions(value_cache, block_tables[s], L, g, dtype)
+            K = gather_positions(key_cache, block_tables[s], L, g, cdt, k_scale)
+            V = gather_positions(value_cache, block_tables[s], L, g, cdt, v_scale)
             for h in range(g * G, (g + 1) * G):
                 out[i, h], _ = _softmax_attend(to_float64(q[s, h], dtype), K, V, sc)
     return out

@@ -384,7 +384,7 @@ def _mutant_no_scale(monkeypatch):
 
 
 def _mutant_swapped_index(monkeypatch):
-    def gather(cache, row, length, kv_head, dtype):
+    def gather(cache, row, length, kv_head, dtype, scale=1.0):
         bs = cache.shape[1]
         t = np.arange(int(length))
         # block and offset roles exchanged (a transposed operand of the indirection)
@@ -396,7 +396,8 @@ def _mutant_swapped_index(monkeypatch):
 def _mutant_off_by_one(monkeypatch):
     orig = opa.gather_positions
     monkeypatch.setattr(opa, "gather_positions",
-                        lambda cache, row, length, g, dt: orig(cache, row, max(length - 1, 1), g, dt))
+                        lambda cache, row, length, g, dt, sc=1.0: orig(cache, row, max(length - 1, 1),
+                                                                       g, dt, sc))
 
 
 def _mutant_no_normalise(monkeypatch):

@@ -47,8 +47,9 @@ def algorithmic_bytes(spec, context_lens: np.ndarray) -> dict:
     Positions >= L and split-K scratch are overhead, not counted.
     """
     L = context_lens.astype(np.int64)
-    esz = 2
-    per_token_head = 2 * spec.head_size * esz
+    esz = 2                                             # q / out element bytes
+    kv_esz = 1 if spec.cache_type == "fp8" else 2       # cache element bytes
+    per_token_head = 2 * spec.head_size * kv_esz
     kv = int(L.sum()) * spec.num_kv_heads * per_token_head
     if spec.shared_prefix_blocks:
         pre = spec.shared_prefix_blocks * spec.block_size
@@ -164,7 +165,9 @@ def cpu_baseline(batch, budget_s: float) -> dict:
             oracle.slot_mapping(batch.block_tables[s:s + 1], batch.context_lens[s:s + 1],
                                 batch.spec.block_size)
             oracle.decode(batch.q, batch.key_cache, batch.value_cache, batch.block_tables,
-                          batch.context_lens, batch.scale, batch.dtype, seqs=[s])
+                          batch.context_lens, batch.scale, batch.dtype, seqs=[s],
+                          cache_dtype=batch.cache_dtype, k_scale=batch.k_scale,
+                          v_scale=batch.v_scale)
             done += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -255,7 +258,14 @@ def main(argv=None) -> int:
     def up16(a):
         return torch.from_numpy(a.view(np.int16)).view(tdt).cuda()
 
-    q, kc, vc = up16(batch.q), up16(batch.key_cache), up16(batch.value_cache)
+    fp8 = spec.cache_type == "fp8"
+    q = up16(batch.q)
+    if fp8:
+        kc = torch.from_numpy(batch.key_cache).cuda()
+        vc = torch.from_numpy(batch.value_cache).cuda()
+    else:
+        kc, vc = up16(batch.key_cache), up16(batch.value_cache)
+    ks, vs = float(batch.k_scale), float(batch.v_scale)
     k_new, v_new = up16(batch.k_new), up16(batch.v_new)
     bt = torch.from_numpy(batch.block_tables).cuda()
     lens = torch.from_numpy(batch.context_lens).cuda()
@@ -270,11 +280,18 @@ def main(argv=None) -> int:
 
     def step(ev0=None, ev1=None):
         pa.decode_slot_mapping(bt, lens, spec.block_size, out=slots, stream=stream)
-        pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
+        if fp8:
+            pa.cache_write_fp8(k_new, v_new, kc, vc, slots, ks, vs, stream=stream)
+        else:
+            pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
-        pa.decode(q, kc, vc, bt, lens, scale, maxlen, out=out,
-                  partition_size=args.partition_size, workspace=ws, stream=stream)
+        if fp8:
+            pa.decode_fp8(q, kc, vc, bt, lens, scale, ks, vs, maxlen, out=out,
+                          partition_size=args.partition_size, workspace=ws, stream=stream)
+        else:
+            pa.decode(q, kc, vc, bt, lens, scale, maxlen, out=out,
+                      partition_size=args.partition_size, workspace=ws, stream=stream)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -323,7 +340,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": spec.dtype,
+        "dtype": spec.dtype if not fp8 else f"fp8_e4m3 K/V, {spec.dtype} q/out",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block tables)",
         "config": {
             "workload": spec.name, "num_seqs": batch.num_seqs, "num_q_heads": spec.num_q_heads,

@@ -117,6 +117,34 @@ PA_API int pa_cache_write(const void* k, const void* v, void* key_cache, void* v
                           int32_t dtype, void* stream);
 
 /*
+ * pa_cache_write_fp8 -- store new tokens' k/v into an FP8 (E4M3) cache.
+ *
+ * The same slot rule as pa_cache_write, for caches that hold one byte per
+ * element: OCP 8-bit floating point E4M3 (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, 0x7F / 0xFF = NaN, largest finite 448).
+ * Each cache tensor has one fp32 scale, and a stored code c stands for
+ * value(c) * scale. For every element x of k (v) the stored code is
+ *   e4m3( fp32(x) / k_scale )     (IEEE fp32 division),
+ * rounded to nearest even, with magnitudes above 448 clamped to 448 and
+ * NaN stored as 0x7F. (FP8 K/V storage: the intelliparadigm article's §4.3
+ * precision table; the format and the per-tensor scale are this library's
+ * reading, since the article fixes neither.)
+ * k, v          : [num_tokens, num_kv_heads, head_size] of src_dtype (device)
+ * key_cache,
+ * value_cache   : uint8 [num_blocks, block_size, num_kv_heads, head_size] (device, updated)
+ * slot_mapping  : int32 [num_tokens] (device); negative / out-of-range slots skip
+ * src_dtype     : PA_DTYPE_FP16 or PA_DTYPE_BF16 (the type of k and v)
+ * k_scale,
+ * v_scale       : finite and > 0
+ * Errors: as pa_cache_write, plus PA_ERR_SHAPE for a scale that is not
+ * finite and positive. num_tokens == 0 enqueues nothing and returns PA_OK.
+ */
+PA_API int pa_cache_write_fp8(const void* k, const void* v, void* key_cache, void* value_cache,
+                              const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                              int32_t src_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs.
  *
  * partition_size < 0 (single pass) needs none (returns 0). partition_size > 0
@@ -196,6 +224,27 @@ PA_API int pa_decode(const void* q, const void* key_cache, const void* value_cac
                      int32_t head_size, int32_t block_size, int64_t num_blocks,
                      int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
                      int32_t dtype, void* workspace, size_t workspace_size, void* stream);
+
+/*
+ * pa_decode_fp8 -- one decode step over FP8 (E4M3) caches.
+ *
+ * Computes what pa_decode computes, with the K rows read as
+ * value(code) * k_scale and the V rows as value(code) * v_scale (the
+ * encoding of pa_cache_write_fp8). q and out keep dtype (PA_DTYPE_FP16 or
+ * PA_DTYPE_BF16); key_cache / value_cache are uint8
+ * [num_blocks, block_size, num_kv_heads, head_size]. The scales are applied
+ * in fp32: k_scale multiplies the logit scale, v_scale the normalised
+ * output. The partitioning, workspace (pa_decode_workspace_size with the
+ * same sizes), stream and error rules are those of pa_decode, plus
+ * PA_ERR_SHAPE for a k_scale or v_scale that is not finite and positive.
+ */
+PA_API int pa_decode_fp8(const void* q, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         float k_scale, float v_scale, void* out, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                         void* workspace, size_t workspace_size, void* stream);
 
 #ifdef __cplusplus
 }

@@ -82,6 +82,103 @@ int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
   return P;
 }
 
+bool valid_scale(float x) { return isfinite(x) && x > 0.f; }
+
+// Host validation shared by the 2-byte and the FP8 cache writes.
+int check_cache_write(const void* k, const void* v, const void* key_cache,
+                      const void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                      int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_size, int32_t dtype) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 0 || block_size < 1 || num_kv_heads < 1 || head_size < 1)
+    return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if ((int64_t)num_kv_heads * head_size > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (head_size % 8 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Shared body of pa_decode and pa_decode_fp8.
+int decode_impl(const void* q, const void* key_cache, const void* value_cache, bool fp8_cache,
+                float k_scale, float v_scale, const int32_t* block_tables,
+                const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                int32_t partition_size, int32_t dtype, void* workspace, size_t workspace_size,
+                void* stream) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (fp8_cache && (!valid_scale(k_scale) || !valid_scale(v_scale))) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+
+  int cus = device_cu_count();
+  if (cus <= 0) cus = kFallbackCUs;
+  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, cus)
+                                    : partition_size;
+  const bool split = P > 0;
+
+  pa::DecodeParams a;
+  a.q = (const uint16_t*)q;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.bt = block_tables;
+  a.lens = context_lens;
+  a.out = (uint16_t*)out;
+  a.ws_m = a.ws_l = a.ws_o = nullptr;
+  // log2(e): logits are kept in base 2; an FP8 cache's K scale folds in here
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  a.v_scale = v_scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.log2_block_size = ilog2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.len_cap = max_context_len;
+  if (split) {
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+    const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, parts);
+    if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
+    char* ws = (char*)workspace;
+    a.ws_m = (float*)(ws + lay.m_off);
+    a.ws_l = (float*)(ws + lay.l_off);
+    a.ws_o = (float*)(ws + lay.o_off);
+    a.part_tokens = P;
+    a.num_parts = (int32_t)parts;
+    // Few (sequence, kv head) pairs: order the grid sequence by sequence.
+    a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
+  } else {
+    a.part_tokens = max_context_len > 0 ? max_context_len : 1;
+    a.num_parts = 1;
+    a.seq_major = 0;
+  }
+  const hipError_t e =
+      pa::launch_decode(a, dtype, fp8_cache, head_size, group, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,20 +216,29 @@ int pa_cache_write(const void* k, const void* v, void* key_cache, void* value_ca
                    const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
                    int32_t block_size, int32_t num_kv_heads, int32_t head_size, int32_t dtype,
                    void* stream) {
-  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
-  if (num_tokens < 0 || num_blocks < 0 || block_size < 1 || num_kv_heads < 1 || head_size < 1)
-    return PA_ERR_SHAPE;
-  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if ((int64_t)num_kv_heads * head_size > INT32_MAX / 2) return PA_ERR_SHAPE;
-  if (head_size % 8 != 0) return PA_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return PA_OK;
-  if (!k || !v || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache))
-    return PA_ERR_UNSUPPORTED;
+  const int st = check_cache_write(k, v, key_cache, value_cache, slot_mapping, num_tokens,
+                                   num_blocks, block_size, num_kv_heads, head_size, dtype);
+  if (st != PA_OK || num_tokens == 0) return st;
   const hipError_t e = pa::launch_cache_write(
       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)key_cache, (uint16_t*)value_cache,
       slot_mapping, num_tokens, num_blocks * (int64_t)block_size, num_kv_heads * head_size,
       (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_cache_write_fp8(const void* k, const void* v, void* key_cache, void* value_cache,
+                       const int32_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                       int32_t src_dtype, float k_scale, float v_scale, void* stream) {
+  const int st = check_cache_write(k, v, key_cache, value_cache, slot_mapping, num_tokens,
+                                   num_blocks, block_size, num_kv_heads, head_size, src_dtype);
+  if (st != PA_OK) return st;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  const hipError_t e = pa::launch_cache_write_fp8(
+      (const uint16_t*)k, (const uint16_t*)v, (uint8_t*)key_cache, (uint8_t*)value_cache,
+      slot_mapping, num_tokens, num_blocks * (int64_t)block_size, num_kv_heads * head_size,
+      src_dtype, k_scale, v_scale, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -159,70 +265,22 @@ int pa_decode(const void* q, const void* key_cache, const void* value_cache,
               int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
               int32_t max_context_len, int32_t partition_size, int32_t dtype, void* workspace,
               size_t workspace_size, void* stream) {
-  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
-  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
-      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
-    return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
-  const int group = num_q_heads / num_kv_heads;
-  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
-  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
-    return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
-    return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
-    return PA_ERR_UNSUPPORTED;
+  return decode_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_tables, context_lens,
+                     scale, out, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
+                     workspace, workspace_size, stream);
+}
 
-  int cus = device_cu_count();
-  if (cus <= 0) cus = kFallbackCUs;
-  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, cus)
-                                    : partition_size;
-  const bool split = P > 0;
-
-  pa::DecodeParams a;
-  a.q = (const uint16_t*)q;
-  a.kc = (const uint16_t*)key_cache;
-  a.vc = (const uint16_t*)value_cache;
-  a.bt = block_tables;
-  a.lens = context_lens;
-  a.out = (uint16_t*)out;
-  a.ws_m = a.ws_l = a.ws_o = nullptr;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.block_size = block_size;
-  a.log2_block_size = ilog2_exact(block_size);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.len_cap = max_context_len;
-  if (split) {
-    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
-    const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, parts);
-    if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
-    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
-    char* ws = (char*)workspace;
-    a.ws_m = (float*)(ws + lay.m_off);
-    a.ws_l = (float*)(ws + lay.l_off);
-    a.ws_o = (float*)(ws + lay.o_off);
-    a.part_tokens = P;
-    a.num_parts = (int32_t)parts;
-    // Few (sequence, kv head) pairs: order the grid sequence by sequence.
-    a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
-  } else {
-    a.part_tokens = max_context_len > 0 ? max_context_len : 1;
-    a.num_parts = 1;
-    a.seq_major = 0;
-  }
-  const hipError_t e =
-      pa::launch_decode(a, dtype, head_size, group, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+int pa_decode_fp8(const void* q, const void* key_cache, const void* value_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                  float k_scale, float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_size, int32_t block_size, int64_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                  int32_t dtype, void* workspace, size_t workspace_size, void* stream) {
+  return decode_impl(q, key_cache, value_cache, true, k_scale, v_scale, block_tables,
+                     context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_size,
+                     block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
+                     dtype, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

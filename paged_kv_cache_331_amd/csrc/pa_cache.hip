@@ -1,4 +1,4 @@
-// Slot mapping and cache write for gfx950.
+// Slot mapping and cache writes (2-byte copy, FP8 E4M3 quantizing) for gfx950.
 //
 // Decode appends the new token's k/v at the next free slot of the sequence's
 // last block before attending ("01. PagedAttention 详解" §4, decode phase);
@@ -48,6 +48,56 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(
   *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(v + src);
 }
 
+// Eight 2-byte source values -> eight E4M3 codes (two words, lowest
+// dimension in the lowest byte): y = fp32(x) / scale (IEEE division),
+// clamped to +-448, rounded to nearest even by v_cvt_pk_fp8_f32; NaN -> 0x7F.
+template <class ST>
+__device__ __forceinline__ u32x2_t encode_fp8x8(uint4 x, float scale) {
+  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  u32x2_t out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      y[2 * j] = Storage<ST>::lo(xw[2 * w + j]) / scale;
+      y[2 * j + 1] = Storage<ST>::hi(xw[2 * w + j]) / scale;
+    }
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], packed, true);
+    uint32_t p = (uint32_t)packed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (y[j] != y[j]) p = (p & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
+    out[w] = p;
+  }
+  return out;
+}
+
+// One thread per 8 elements of a token's [Hkv, D] row, for k and v alike.
+template <class ST>
+__global__ __launch_bounds__(kWriteThreads) void cache_write_fp8_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens,
+    int64_t num_slots, int32_t row_elems, float k_scale, float v_scale) {
+  const int chunks = row_elems / 8;
+  const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+  const int64_t tok = gid / chunks;
+  if (tok >= num_tokens) return;
+  const int c = (int)(gid - tok * chunks);
+  const int32_t slot = slots[tok];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int64_t src = tok * row_elems + (int64_t)c * 8;
+  const int64_t dst = (int64_t)slot * row_elems + (int64_t)c * 8;
+  *reinterpret_cast<u32x2_t*>(kc + dst) =
+      encode_fp8x8<ST>(*reinterpret_cast<const uint4*>(k + src), k_scale);
+  *reinterpret_cast<u32x2_t*>(vc + dst) =
+      encode_fp8x8<ST>(*reinterpret_cast<const uint4*>(v + src), v_scale);
+}
+
 }  // namespace
 
 hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq, const int32_t* lens,
@@ -69,6 +119,29 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, uint16_t* kc
   if (grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(cache_write_kernel, dim3((uint32_t)grid), dim3(kWriteThreads), 0, stream, k, v,
                      kc, vc, slots, num_tokens, num_slots, row_elems);
+  return hipGetLastError();
+}
+
+}  // namespace pa
+
+namespace pa {
+
+hipError_t launch_cache_write_fp8(const uint16_t* k, const uint16_t* v, uint8_t* kc, uint8_t* vc,
+                                  const int32_t* slots, int32_t num_tokens, int64_t num_slots,
+                                  int32_t row_elems, int src_dtype, float k_scale, float v_scale,
+                                  hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t total = (int64_t)num_tokens * (row_elems / 8);
+  const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
+  if (grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
+  if (src_dtype == 0)
+    hipLaunchKernelGGL(cache_write_fp8_kernel<Fp16>, dim3((uint32_t)grid), dim3(kWriteThreads), 0,
+                       stream, k, v, kc, vc, slots, num_tokens, num_slots, row_elems, k_scale,
+                       v_scale);
+  else
+    hipLaunchKernelGGL(cache_write_fp8_kernel<Bf16>, dim3((uint32_t)grid), dim3(kWriteThreads), 0,
+                       stream, k, v, kc, vc, slots, num_tokens, num_slots, row_elems, k_scale,
+                       v_scale);
   return hipGetLastError();
 }
 

@@ -44,11 +44,14 @@ union Vec16 {
   uint32_t w[4];
 };
 
-template <class DT, int D, int G>
+template <class DT, class KT, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   using S = Storage<DT>;
+  using KV = Kv<DT, KT>;
+  using elem = typename KV::elem;
+  using row_t = typename KV::row;
   constexpr int NW = kDecodeWaves;
-  constexpr int LPR = D / 8;           // lanes per token row (16 B per lane)
+  constexpr int LPR = D / 8;           // lanes per token row (8 dimensions per lane)
   constexpr int ROWS = 64 / LPR;       // token rows per load instruction
   constexpr int TG = kTile / ROWS;     // load instructions per tile and tensor
   constexpr int DL = 8;                // dimensions held per lane
@@ -90,6 +93,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   const int col = lane % LPR;
   const int64_t tok_stride = (int64_t)Hkv * D;        // elements between slots
   const int64_t lane_elem = row * tok_stride + (int64_t)g * D + col * 8;
+  const elem* kc = static_cast<const elem*>(a.kc);
+  const elem* vc = static_cast<const elem*>(a.vc);
 
   // q slices of the G query heads of this kv head (raw storage words).
   uint32_t qw[G][4];
@@ -136,22 +141,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
       const int off0 = ts & (bs - 1);            // tile never straddles a block (bs % 16 == 0)
       const int64_t base = ((int64_t)blk * bs + off0) * tok_stride + lane_elem;
 
-      u32x4_t kr[TG], vr[TG];
+      row_t kr[TG], vr[TG];
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) kr[tg] = load_stream16(a.kc + base + tg * ROWS * tok_stride);
+      for (int tg = 0; tg < TG; ++tg) kr[tg] = KV::load(kc + base + tg * ROWS * tok_stride);
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) vr[tg] = load_stream16(a.vc + base + tg * ROWS * tok_stride);
+      for (int tg = 0; tg < TG; ++tg) vr[tg] = KV::load(vc + base + tg * ROWS * tok_stride);
 
       float lg[G][TG];
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d = S::dot2(qw[h][e], kr[tg][e], d);
-          lg[h][tg] = row_sum<LPR>(d) * sl2;
-        }
+        for (int tg = 0; tg < TG; ++tg) lg[h][tg] = row_sum<LPR>(KV::dot(qw[h], kr[tg], 0.f)) * sl2;
 
       if (ts + kTile > end) {                    // tail tile: mask positions >= end
 #pragma unroll
@@ -159,10 +159,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
           const bool ok = ts + tg * ROWS + row < end;
 #pragma unroll
           for (int h = 0; h < G; ++h) lg[h][tg] = ok ? lg[h][tg] : -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[tg][e] = ok ? vr[tg][e] : 0u;
+          vr[tg] = ok ? vr[tg] : KV::zero();
         }
       }
+      float vx[TG][8];
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) KV::widen(vr[tg], vx[tg]);
 
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -185,10 +187,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[h][2 * e] = fmaf(pr[tg], S::lo(vr[tg][e]), acc[h][2 * e]);
-            acc[h][2 * e + 1] = fmaf(pr[tg], S::hi(vr[tg][e]), acc[h][2 * e + 1]);
-          }
+          for (int d = 0; d < DL; ++d) acc[h][d] = fmaf(pr[tg], vx[tg][d], acc[h][d]);
       }
     }
   }
@@ -241,6 +240,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
       num = fmaf(c, s_part[w][h][d], num);
       den = fmaf(c, s_part[w][h][D + 1], den);
     }
+    num *= a.v_scale;                                   // 1 unless the cache is FP8
     const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
     if (np == 1) {
       a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
@@ -331,12 +331,12 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   *reinterpret_cast<uint2*>(a.out + oh * D + c * 4) = packed;
 }
 
-template <class DT, int D, int G>
+template <class DT, class KT, int D, int G>
 hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   const uint64_t nwg = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>), dim3((uint32_t)nwg),
+  hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G>), dim3((uint32_t)nwg),
                      dim3(kDecodeWaves * 64), 0, st, a);
   if (a.num_parts == 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
@@ -347,32 +347,35 @@ hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class DT, int D>
+template <class DT, class KT, int D>
 hipError_t launch_d(const DecodeParams& a, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_dg<DT, D, 1>(a, st);
-    case 2: return launch_dg<DT, D, 2>(a, st);
-    case 4: return launch_dg<DT, D, 4>(a, st);
-    case 8: return launch_dg<DT, D, 8>(a, st);
+    case 1: return launch_dg<DT, KT, D, 1>(a, st);
+    case 2: return launch_dg<DT, KT, D, 2>(a, st);
+    case 4: return launch_dg<DT, KT, D, 4>(a, st);
+    case 8: return launch_dg<DT, KT, D, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <class DT>
+template <class DT, class KT>
 hipError_t launch_t(const DecodeParams& a, int head_size, int group, hipStream_t st) {
   switch (head_size) {
-    case 64: return launch_d<DT, 64>(a, group, st);
-    case 128: return launch_d<DT, 128>(a, group, st);
+    case 64: return launch_d<DT, KT, 64>(a, group, st);
+    case 128: return launch_d<DT, KT, 128>(a, group, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group,
-                         hipStream_t stream) {
-  return dtype == 0 ? launch_t<Fp16>(a, head_size, group, stream)
-                    : launch_t<Bf16>(a, head_size, group, stream);
+hipError_t launch_decode(const DecodeParams& a, int dtype, bool fp8_cache, int head_size,
+                         int group, hipStream_t stream) {
+  if (fp8_cache)
+    return dtype == 0 ? launch_t<Fp16, Fp8>(a, head_size, group, stream)
+                      : launch_t<Bf16, Fp8>(a, head_size, group, stream);
+  return dtype == 0 ? launch_t<Fp16, Fp16>(a, head_size, group, stream)
+                    : launch_t<Bf16, Bf16>(a, head_size, group, stream);
 }
 
 }  // namespace pa

@@ -1,7 +1,8 @@
 // Device-side helpers for the gfx950 paged-attention kernels: storage-type
-// traits (fp16 / bf16 as raw 16-bit words), packed dot products on the
-// v_dot2 instructions, DPP reductions inside 8-lane token rows, and fp32 ->
-// storage rounding.
+// traits (fp16 / bf16 as raw 16-bit words), cache-element traits (the
+// query's 2-byte type, or FP8 E4M3 codes), packed dot products on the v_dot2
+// instructions, DPP reductions inside token rows, and fp32 -> storage
+// rounding.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,6 +15,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct Fp16 {};
 struct Bf16 {};
+struct Fp8 {};   // OCP E4M3 codes (cache element type only)
 
 template <class DT> struct Storage;
 
@@ -80,12 +82,84 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// 16-byte load marked non-temporal: K/V rows are streamed once per step, so
-// they should not displace anything else from the caches.
-__device__ __forceinline__ u32x4_t load_stream16(const uint16_t* p) {
+// Loads marked non-temporal: K/V rows are streamed once per step, so they
+// should not displace anything else from the caches.
+__device__ __forceinline__ u32x4_t load_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
+__device__ __forceinline__ u32x2_t load_stream8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
+// The slice of one cached K or V row a lane holds: 8 consecutive dimensions.
+// QT is the query's type (fp16 / bf16), KT the cache element type.
+template <class QT, class KT> struct Kv;
+
+// Cache in the query's 2-byte type: 16 bytes per lane.
+template <class QT> struct Kv<QT, QT> {
+  typedef uint16_t elem;
+  typedef u32x4_t row;
+  static __device__ __forceinline__ row load(const elem* p) { return load_stream16(p); }
+  // acc + q . k over the 8 dimensions (q as 4 packed pairs of QT).
+  static __device__ __forceinline__ float dot(const uint32_t (&q)[4], row k, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = Storage<QT>::dot2(q[e], k[e], acc);
+    return acc;
+  }
+  static __device__ __forceinline__ void widen(row v, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = Storage<QT>::lo(v[e]);
+      x[2 * e + 1] = Storage<QT>::hi(v[e]);
+    }
+  }
+  static __device__ __forceinline__ row zero() { return row{0u, 0u, 0u, 0u}; }
+};
+
+// Two E4M3 codes (the low or high 16 bits of w, lower address first) as a
+// pair of QT. Every E4M3 value is exact in fp16 and in bf16, so the unit
+// scale leaves the conversion exact.
+template <class QT> struct Fp8Pair;
+template <> struct Fp8Pair<Fp16> {
+  template <bool HIGH> static __device__ __forceinline__ uint32_t get(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
+  }
+};
+template <> struct Fp8Pair<Bf16> {
+  template <bool HIGH> static __device__ __forceinline__ uint32_t get(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+  }
+};
+
+// FP8 E4M3 cache: 8 bytes per lane. The tensor's scale is applied outside
+// (folded into the logit scale for K, into the output for V).
+template <class QT> struct Kv<QT, Fp8> {
+  typedef uint8_t elem;
+  typedef u32x2_t row;
+  static __device__ __forceinline__ row load(const elem* p) { return load_stream8(p); }
+  static __device__ __forceinline__ float dot(const uint32_t (&q)[4], row k, float acc) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      acc = Storage<QT>::dot2(q[2 * w], Fp8Pair<QT>::template get<false>(k[w]), acc);
+      acc = Storage<QT>::dot2(q[2 * w + 1], Fp8Pair<QT>::template get<true>(k[w]), acc);
+    }
+    return acc;
+  }
+  static __device__ __forceinline__ void widen(row v, float (&x)[8]) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
+      x[4 * w] = lo[0];
+      x[4 * w + 1] = lo[1];
+      x[4 * w + 2] = hi[0];
+      x[4 * w + 3] = hi[1];
+    }
+  }
+  static __device__ __forceinline__ row zero() { return row{0u, 0u}; }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

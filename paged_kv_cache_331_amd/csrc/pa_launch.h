@@ -10,15 +10,16 @@ namespace pa {
 // Everything one decode launch needs. Pointers are device pointers.
 struct DecodeParams {
   const uint16_t* q;        // [B, Hq, D]
-  const uint16_t* kc;       // [NB, bs, Hkv, D]
-  const uint16_t* vc;       // [NB, bs, Hkv, D]
+  const void* kc;           // [NB, bs, Hkv, D], 2-byte elements or FP8 E4M3 codes
+  const void* vc;           // [NB, bs, Hkv, D]
   const int32_t* bt;        // [B, MB]
   const int32_t* lens;      // [B]
   uint16_t* out;            // [B, Hq, D]
   float* ws_m;              // split-K partials: running max (log2 units) [B, Hq, P]
   float* ws_l;              //                   exp-sum                  [B, Hq, P]
   float* ws_o;              //                   weighted V sum           [B, Hq, P, D]
-  float scale_log2;         // scale * log2(e): logits are kept in base-2 units
+  float scale_log2;         // scale * k_scale * log2(e): logits are kept in base-2 units
+  float v_scale;            // multiplies the weighted V sum (FP8 cache scale, else 1)
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -39,8 +40,9 @@ constexpr int kDecodeWaves = 4;
 constexpr int kReduceThreads = 256;
 
 // One decode step: the partition kernel, then (num_parts > 1) the combine.
-hipError_t launch_decode(const DecodeParams& a, int dtype, int head_size, int group,
-                         hipStream_t stream);
+// dtype: q / out type (0 fp16, 1 bf16); fp8_cache: the caches hold E4M3 codes.
+hipError_t launch_decode(const DecodeParams& a, int dtype, bool fp8_cache, int head_size,
+                         int group, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq,
                                const int32_t* lens, int32_t num_seqs, int32_t block_size,
@@ -49,5 +51,11 @@ hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq,
 hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, uint16_t* kc, uint16_t* vc,
                               const int32_t* slots, int32_t num_tokens, int64_t num_slots,
                               int32_t row_elems, hipStream_t stream);
+
+// Quantizing write into an FP8 E4M3 cache: code = e4m3(fp32(x) / scale).
+hipError_t launch_cache_write_fp8(const uint16_t* k, const uint16_t* v, uint8_t* kc, uint8_t* vc,
+                                  const int32_t* slots, int32_t num_tokens, int64_t num_slots,
+                                  int32_t row_elems, int src_dtype, float k_scale, float v_scale,
+                                  hipStream_t stream);
 
 }  // namespace pa

@@ -36,6 +36,11 @@ SIGNATURES = {
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_cache_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+                                          _i32, _f32, _f32, _vp]),
+    "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32, _i32,
+                                     _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz,
+                                     _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -127,6 +132,22 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, key_cache: torch.Tensor,
     _check("pa_cache_write", st)
 
 
+def cache_write_fp8(k: torch.Tensor, v: torch.Tensor, key_cache: torch.Tensor,
+                    value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                    v_scale: float, stream=None) -> None:
+    """Quantize k[i], v[i] ([T, Hkv, D], fp16/bf16) into the uint8 E4M3 caches at slot_mapping[i]."""
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+    NB, bs, Hkv, D = key_cache.shape
+    T = k.shape[0]
+    st = load().pa_cache_write_fp8(_dev(k, "k"), _dev(v, "v"), _dev(key_cache, "key_cache"),
+                                   _dev(value_cache, "value_cache"),
+                                   _dev(slot_mapping, "slot_mapping"), T, NB, bs, Hkv, D,
+                                   dtype_code(k.dtype), float(k_scale), float(v_scale),
+                                   _stream(stream))
+    _check("pa_cache_write_fp8", st)
+
+
 def decode_workspace_size(num_seqs: int, num_q_heads: int, head_size: int,
                           max_context_len: int, partition_size: int = 0) -> int:
     return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, head_size,
@@ -161,4 +182,33 @@ def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                           B, Hq, Hkv, D, bs, NB, MB, int(max_context_len), int(partition_size),
                           dtype_code(q.dtype), ws_ptr, ws_len, _stream(stream))
     _check("pa_decode", st)
+    return out
+
+
+def decode_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+               k_scale: float, v_scale: float, max_context_len: int,
+               out: Optional[torch.Tensor] = None, partition_size: int = 0,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode step over uint8 E4M3 caches with per-tensor scales; ``out`` has q's dtype."""
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().pa_decode_fp8(_dev(q, "q"), _dev(key_cache, "key_cache"),
+                              _dev(value_cache, "value_cache"),
+                              _dev(block_tables, "block_tables"),
+                              _dev(context_lens, "context_lens"), float(scale), float(k_scale),
+                              float(v_scale), _dev(out, "out"), B, Hq, Hkv, D, bs, NB, MB,
+                              int(max_context_len), int(partition_size), dtype_code(q.dtype),
+                              ws_ptr, ws_len, _stream(stream))
+    _check("pa_decode_fp8", st)
     return out

@@ -15,7 +15,11 @@ A sequence of L tokens owns ceil(L / block_size) blocks ("PagedAttention 机制"
 wiki, §5.3.2, the allocation rule of its BlockTable sketch).
 
 Values are returned as numpy ``uint16`` bit patterns plus a dtype tag
-("fp16" / "bf16"); both sides upcast them with their own code.
+("fp16" / "bf16"); both sides upcast them with their own code. A workload
+with an FP8 cache ("fp8" cache dtype) keeps q and the new token's k/v in the
+2-byte type and fills the pools with uint8 E4M3 codes of N(0,1) / scale,
+produced by torch's float8_e4m3fn conversion (input preparation only; the
+oracle has its own encoder).
 """
 from __future__ import annotations
 
@@ -58,6 +62,12 @@ class WorkloadSpec:
     partition_size: int = 0            # split-K partition the workload is quoted with (0: auto)
     cache_write: bool = True           # one new token per sequence written before attention
     seed_index: int = 0                # second word of the seed key
+    cache_dtype: str = ""              # "" = dtype; "fp8" = E4M3 codes with kv_scale
+    kv_scale: float = 2.0 ** -5        # fp32 scale of both FP8 cache tensors
+
+    @property
+    def cache_type(self) -> str:
+        return self.cache_dtype or self.dtype
 
     @property
     def group_size(self) -> int:
@@ -99,9 +109,20 @@ CONFIGS = {
         name="prefix_shared_write", num_seqs=128, num_q_heads=32, num_kv_heads=8, head_size=128,
         block_size=32, dtype="bf16", lengths="uniform", len_lo=16, len_hi=512,
         shared_prefix_blocks=32, seed_index=5),
+    # FP8 (E4M3) caches of the MHA and GQA batches: same shapes and length
+    # laws, q / out / new k, v in the 2-byte type.
+    "llama2_7b_mha_fp8": WorkloadSpec(
+        name="llama2_7b_mha_fp8", num_seqs=64, num_q_heads=32, num_kv_heads=32, head_size=128,
+        block_size=16, dtype="fp16", lengths="uniform", len_lo=512, len_hi=2048,
+        seed_index=6, cache_dtype="fp8"),
+    "gqa_8b_fp8": WorkloadSpec(
+        name="gqa_8b_fp8", num_seqs=256, num_q_heads=32, num_kv_heads=8, head_size=128,
+        block_size=16, dtype="bf16", lengths="lognormal", len_lo=16, len_hi=4096,
+        len_median=1000.0, len_sigma=1.0, seed_index=7, cache_dtype="fp8"),
 }
 CONFIG_ORDER = ("tiny_write", "llama2_7b_mha", "gqa_8b", "long_context_splitk",
                 "prefix_shared_write")
+FP8_ORDER = ("llama2_7b_mha_fp8", "gqa_8b_fp8")
 
 
 @dataclass
@@ -110,8 +131,8 @@ class Batch:
 
     spec: WorkloadSpec
     q: np.ndarray              # uint16 [B, Hq, D]
-    key_cache: np.ndarray      # uint16 [NB, bs, Hkv, D]
-    value_cache: np.ndarray    # uint16 [NB, bs, Hkv, D]
+    key_cache: np.ndarray      # uint16 [NB, bs, Hkv, D] (uint8 E4M3 codes for an FP8 cache)
+    value_cache: np.ndarray    # same as key_cache
     block_tables: np.ndarray   # int32 [B, MB]
     context_lens: np.ndarray   # int32 [B]
     k_new: np.ndarray          # uint16 [B, Hkv, D]  (the new token's key)
@@ -124,6 +145,18 @@ class Batch:
     @property
     def dtype(self) -> str:
         return self.spec.dtype
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.spec.cache_type
+
+    @property
+    def k_scale(self) -> np.float32:
+        return np.float32(self.spec.kv_scale if self.cache_dtype == "fp8" else 1.0)
+
+    @property
+    def v_scale(self) -> np.float32:
+        return self.k_scale
 
     @property
     def num_seqs(self) -> int:
@@ -155,7 +188,7 @@ def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def nan_bits(dtype: str) -> int:
     """A quiet-NaN bit pattern of the storage type (used to poison memory)."""
-    return {"fp16": 0x7E00, "bf16": 0x7FC0}[dtype]
+    return {"fp16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}[dtype]
 
 
 def _threads() -> int:
@@ -192,6 +225,14 @@ def fill_normal(shape: Sequence[int], dtype: str, key: Sequence[int]) -> np.ndar
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(nch)))
     return out.reshape(shape)
+
+
+def fill_fp8(shape: Sequence[int], scale: float, key: Sequence[int]) -> np.ndarray:
+    """E4M3 codes of N(0,1) / scale (torch's float8_e4m3fn conversion), uint8."""
+    import torch
+    bits16 = fill_normal(shape, "bf16", key)     # a seeded N(0,1) draw, as bf16 bits
+    x = torch.from_numpy(bits16.view(np.int16)).view(torch.bfloat16).float() / float(scale)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(shape)
 
 
 def draw_lengths(spec: WorkloadSpec, rng: np.random.Generator, num_seqs: int) -> np.ndarray:
@@ -270,13 +311,17 @@ def make_batch(spec: WorkloadSpec, *, lengths: Optional[Sequence[int]] = None,
     dt = spec.dtype
     if values:
         q = fill_normal((B, Hq, D), dt, key + [_STREAM_Q])
-        kc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_K])
-        vc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_V])
+        if spec.cache_type == "fp8":
+            kc = fill_fp8((NB, bs, Hkv, D), spec.kv_scale, key + [_STREAM_K])
+            vc = fill_fp8((NB, bs, Hkv, D), spec.kv_scale, key + [_STREAM_V])
+        else:
+            kc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_K])
+            vc = fill_normal((NB, bs, Hkv, D), dt, key + [_STREAM_V])
         k_new = fill_normal((B, Hkv, D), dt, key + [_STREAM_KNEW])
         v_new = fill_normal((B, Hkv, D), dt, key + [_STREAM_VNEW])
     else:
         q = np.empty((0, Hq, D), np.uint16)
-        kc = vc = np.empty((0, bs, Hkv, D), np.uint16)
+        kc = vc = np.empty((0, bs, Hkv, D), np.uint8 if spec.cache_type == "fp8" else np.uint16)
         k_new = v_new = np.empty((0, Hkv, D), np.uint16)
     scale = np.float32(1.0 / math.sqrt(D))
     return Batch(spec=spec, q=q, key_cache=kc, value_cache=vc, block_tables=tables,
@@ -293,6 +338,6 @@ def poison_unused_blocks(batch: Batch) -> None:
     """Fill every physical block no table uses (including the pad block) with NaN."""
     mask = np.ones(batch.num_blocks, dtype=bool)
     mask[batch.used_blocks] = False
-    nb = nan_bits(batch.dtype)
+    nb = nan_bits(batch.cache_dtype)
     batch.key_cache[mask] = nb
     batch.value_cache[mask] = nb

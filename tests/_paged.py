@@ -39,14 +39,26 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def up8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def down8(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().cpu().numpy()
+
+
 class Device:
     """The batch's arrays on the GPU."""
 
     def __init__(self, b: wl.Batch):
         dt = b.dtype
         self.q = up16(b.q, dt)
-        self.kc = up16(b.key_cache, dt)
-        self.vc = up16(b.value_cache, dt)
+        if b.cache_dtype == "fp8":
+            self.kc = up8(b.key_cache)
+            self.vc = up8(b.value_cache)
+        else:
+            self.kc = up16(b.key_cache, dt)
+            self.vc = up16(b.value_cache, dt)
         self.bt = up32(b.block_tables)
         self.lens = up32(b.context_lens)
         self.k_new = up16(b.k_new, dt)
@@ -56,10 +68,17 @@ class Device:
 def gpu_step(b: wl.Batch, d: Device, *, write: bool, partition_size: int = 0):
     """Slot mapping + cache write (optional) + decode; returns (slots, out)."""
     slots = pa.decode_slot_mapping(d.bt, d.lens, b.spec.block_size)
-    if write:
-        pa.cache_write(d.k_new, d.v_new, d.kc, d.vc, slots)
-    out = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len,
-                    partition_size=partition_size)
+    if b.cache_dtype == "fp8":
+        if write:
+            pa.cache_write_fp8(d.k_new, d.v_new, d.kc, d.vc, slots, float(b.k_scale),
+                               float(b.v_scale))
+        out = pa.decode_fp8(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), float(b.k_scale),
+                            float(b.v_scale), b.max_context_len, partition_size=partition_size)
+    else:
+        if write:
+            pa.cache_write(d.k_new, d.v_new, d.kc, d.vc, slots)
+        out = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len,
+                        partition_size=partition_size)
     torch.cuda.synchronize()
     return slots, out
 
@@ -68,8 +87,23 @@ def oracle_caches(b: wl.Batch, write: bool):
     if not write:
         return b.key_cache, b.value_cache, None
     slots = oracle.slot_mapping(b.block_tables, b.context_lens, b.spec.block_size)
-    kc, vc = oracle.cache_write(b.key_cache, b.value_cache, b.k_new, b.v_new, slots)
+    if b.cache_dtype == "fp8":
+        kc, vc = oracle.cache_write_fp8(b.key_cache, b.value_cache, b.k_new, b.v_new, slots,
+                                        b.dtype, b.k_scale, b.v_scale)
+    else:
+        kc, vc = oracle.cache_write(b.key_cache, b.value_cache, b.k_new, b.v_new, slots)
     return kc, vc, slots
+
+
+def oracle_decode(b: wl.Batch, kc, vc, seqs=None):
+    """The oracle's output for the batch with the given caches (any cache type)."""
+    return oracle.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=seqs,
+                         cache_dtype=b.cache_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
+
+
+def oracle_decode_one(b: wl.Batch, kc, vc, s, h):
+    return oracle.decode_one(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype, s, h,
+                             cache_dtype=b.cache_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
 
 
 def max_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
@@ -79,7 +113,7 @@ def max_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
 def poison_tails(b: wl.Batch, write: bool) -> None:
     """NaN into every slot at a position >= L inside each sequence's last block
     (after the newest token, which the write fills)."""
-    nb = wl.nan_bits(b.dtype)
+    nb = wl.nan_bits(b.cache_dtype)
     bs = b.spec.block_size
     for s in range(b.num_seqs):
         L = int(b.context_lens[s])

@@ -28,7 +28,8 @@ def lib():
 def test_header_declares_expected_api():
     assert _declared() == sorted(["pa_abi_version", "pa_status_string", "pa_decode_slot_mapping",
                                   "pa_cache_write", "pa_decode_workspace_size",
-                                  "pa_decode_partition_size", "pa_decode"])
+                                  "pa_decode_partition_size", "pa_decode", "pa_cache_write_fp8",
+                                  "pa_decode_fp8"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -161,3 +162,55 @@ def test_auto_partition_rule(lib, B, Hkv, maxlen, cus, expect):
 def test_auto_partition_invalid(lib):
     assert pa.decode_partition_size(-1, 8, 10, 256) == 0
     assert pa.decode_partition_size(1, 0, 10, 256) == 0
+
+
+def _decode_fp8(**kw):
+    a = dict(q=16, kc=16, vc=16, bt=16, lens=16, scale=0.125, ks=1.0, vs=1.0, out=16, B=2, Hq=4,
+             Hkv=4, D=128, bs=16, NB=10, MB=4, maxlen=64, P=-1, dtype=F, ws=None, wss=0,
+             stream=None)
+    a.update(kw)
+    return pa.load().pa_decode_fp8(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"],
+                                   a["ks"], a["vs"], a["out"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                   a["bs"], a["NB"], a["MB"], a["maxlen"], a["P"], a["dtype"],
+                                   a["ws"], a["wss"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3),
+    (dict(ks=0.0), -2),
+    (dict(vs=-1.0), -2),
+    (dict(ks=float("nan")), -2),
+    (dict(vs=float("inf")), -2),
+    (dict(D=96), -4),
+    (dict(q=None), -1),
+    (dict(P=16, ws=None, wss=0), -5),
+])
+def test_decode_fp8_validation(lib, kw, code):
+    assert _decode_fp8(**kw) == code
+
+
+def _write_fp8(**kw):
+    a = dict(k=16, v=16, kc=16, vc=16, slots=16, T=4, NB=8, bs=16, Hkv=2, D=64, dtype=F, ks=1.0,
+             vs=1.0, stream=None)
+    a.update(kw)
+    return pa.load().pa_cache_write_fp8(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["T"],
+                                        a["NB"], a["bs"], a["Hkv"], a["D"], a["dtype"], a["ks"],
+                                        a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3),
+    (dict(T=-1), -2),
+    (dict(ks=0.0), -2),
+    (dict(vs=float("nan")), -2),
+    (dict(D=12), -4),
+    (dict(kc=None), -1),
+    (dict(vc=8), -4),
+])
+def test_cache_write_fp8_validation(lib, kw, code):
+    assert _write_fp8(**kw) == code
+
+
+def test_fp8_zero_work_is_ok(lib):
+    assert _write_fp8(T=0, k=None, v=None, kc=None, vc=None, slots=None) == 0
+    assert _decode_fp8(B=0, q=None, out=None) == 0

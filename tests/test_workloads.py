@@ -3,6 +3,8 @@ and round-to-nearest-even storage rounding (CPU only)."""
 import math
 
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -102,3 +104,17 @@ def test_explicit_lengths_and_poison():
     used = set(b.used_blocks.tolist())
     for blk in range(b.num_blocks):
         assert np.all(b.key_cache[blk] == nb) == (blk not in used)
+
+
+@pytest.mark.parametrize("name", wl.FP8_ORDER)
+def test_fp8_pools_are_scaled_normal_codes(name):
+    """FP8 workloads: uint8 E4M3 pools with no NaN code whose dequantized values
+    (code * scale) look like N(0, 1); q and the new k/v stay 2-byte."""
+    spec = wl.small_variant(name, 4)
+    b = wl.make_batch(spec)
+    assert b.key_cache.dtype == np.uint8 and b.value_cache.dtype == np.uint8
+    assert b.q.dtype == np.uint16 and b.k_new.dtype == np.uint16
+    for pool in (b.key_cache, b.value_cache):
+        assert not np.any((pool & 0x7F) == 0x7F)
+        x = oracle.e4m3_decode(pool[:64]) * float(b.k_scale)
+        assert abs(x.mean()) < 0.02 and abs(x.std() - 1) < 0.03

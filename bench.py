@@ -222,6 +222,8 @@ def main(argv=None) -> int:
                     help="0 automatic, <0 single pass, >0 split-K partition tokens")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="decode a shared-prefix batch with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only time a 1 GiB device copy (the counter calibration run)")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -272,8 +274,16 @@ def main(argv=None) -> int:
     out = torch.empty_like(q)
     slots = torch.empty(batch.num_seqs, dtype=torch.int32, device="cuda")
     maxlen = batch.max_context_len
-    ws_bytes = pa.decode_workspace_size(batch.num_seqs, spec.num_q_heads, spec.head_size,
-                                        maxlen, args.partition_size)
+    # A batch whose tables share a prefix (the scheduler knows it: one physical
+    # copy referenced by every sequence) is decoded with the cascade.
+    cascade = spec.shared_prefix_blocks > 0 and not args.no_cascade and not fp8
+    if cascade:
+        ws_bytes = pa.decode_cascade_workspace_size(batch.num_seqs, spec.num_q_heads,
+                                                    spec.head_size, spec.block_size, maxlen,
+                                                    spec.shared_prefix_blocks, args.partition_size)
+    else:
+        ws_bytes = pa.decode_workspace_size(batch.num_seqs, spec.num_q_heads, spec.head_size,
+                                            maxlen, args.partition_size)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     scale = float(batch.scale)
     stream = torch.cuda.current_stream()
@@ -289,6 +299,10 @@ def main(argv=None) -> int:
         if fp8:
             pa.decode_fp8(q, kc, vc, bt, lens, scale, ks, vs, maxlen, out=out,
                           partition_size=args.partition_size, workspace=ws, stream=stream)
+        elif cascade:
+            pa.decode_cascade(q, kc, vc, bt, lens, scale, maxlen, spec.shared_prefix_blocks,
+                              out=out, partition_size=args.partition_size, workspace=ws,
+                              stream=stream)
         else:
             pa.decode(q, kc, vc, bt, lens, scale, maxlen, out=out,
                       partition_size=args.partition_size, workspace=ws, stream=stream)
@@ -351,7 +365,9 @@ def main(argv=None) -> int:
             "partition_tokens_used": (args.partition_size if args.partition_size != 0 else
                                       pa.decode_partition_size(batch.num_seqs, spec.num_kv_heads,
                                                                maxlen)),
-            "step": "slot mapping + cache write + decode", "parallelism": "single GPU"},
+            "step": "slot mapping + cache write + " + ("cascade decode (shared prefix)"
+                                                       if cascade else "decode"),
+            "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm", "kernel": "pa_decode (events around the call on its stream)",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

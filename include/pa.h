@@ -246,6 +246,58 @@ PA_API int pa_decode_fp8(const void* q, const void* key_cache, const void* value
                          int32_t max_context_len, int32_t partition_size, int32_t dtype,
                          void* workspace, size_t workspace_size, void* stream);
 
+/*
+ * pa_decode_cascade_workspace_size -- workspace bytes of pa_decode_cascade.
+ *
+ * Room for the fp32 partials of ceil(prefix_len / 256) prefix chunks plus the
+ * partitions of the positions past the prefix (as pa_decode_workspace_size
+ * counts them for max_context_len - prefix_len tokens), per (sequence, query
+ * head), with prefix_len = shared_prefix_blocks * block_size. With
+ * shared_prefix_blocks == 0 it equals pa_decode_workspace_size. Pure host
+ * arithmetic; 0 for invalid sizes.
+ */
+PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_size, int32_t block_size,
+                                               int32_t max_context_len,
+                                               int32_t shared_prefix_blocks,
+                                               int32_t partition_size);
+
+/*
+ * pa_decode_cascade -- pa_decode for a batch whose tables share a prefix.
+ *
+ * Precondition: block_tables[s][0 .. shared_prefix_blocks-1] are the same
+ * physical blocks for every sequence s (a prompt prefix stored once and
+ * referenced by every request, "01. PagedAttention 详解" §6). The result is
+ * then what pa_decode returns (same arguments, same error rules), computed
+ * as:
+ *   - the shared prefix, positions [0, prefix_len), prefix_len =
+ *     shared_prefix_blocks * block_size: every (sequence, query head) row of
+ *     a kv head against one read of the prefix's K/V, as dense matrix
+ *     products on the matrix cores (keys at or past a sequence's own length
+ *     are masked, so a sequence shorter than the prefix is still exact);
+ *   - each sequence's positions [prefix_len, L) on the ordinary partition
+ *     kernel (partition_size as in pa_decode, applied to that range);
+ *   - the combine of both kinds of partials, as in the split path.
+ * The softmax weights enter the matrix products rounded to the query's 2-byte
+ * type; accumulation stays fp32. The prefix is read through row 0 of
+ * block_tables. If the precondition does not hold the output rows of the
+ * sequences whose prefix differs are undefined (no fault: every block id read
+ * is range-checked).
+ * shared_prefix_blocks : 0 .. max_blocks_per_seq (0 = a plain pa_decode call)
+ * workspace            : at least pa_decode_cascade_workspace_size(...) bytes,
+ *                        256-byte aligned; scratch for this call only
+ * Errors: those of pa_decode, and PA_ERR_SHAPE for shared_prefix_blocks out
+ * of range. Caches of the query's 2-byte type only.
+ */
+PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* value_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                             int64_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t shared_prefix_blocks,
+                             int32_t partition_size, int32_t dtype, void* workspace,
+                             size_t workspace_size, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

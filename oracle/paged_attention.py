@@ -49,7 +49,7 @@ import numpy as np
 __all__ = [
     "to_float64", "physical_slot", "slot_mapping", "cache_write",
     "gather_positions", "decode", "decode_one", "attention_weights",
-    "decode_partitioned", "blocks_needed",
+    "decode_partitioned", "decode_two_level", "blocks_needed",
 ]
 
 
@@ -228,6 +228,52 @@ def decode_partitioned(q: np.ndarray, key_cache: np.ndarray, value_cache: np.nda
                     w = np.exp(logits - m_p)
                     Z_p = w.sum()
                     parts.append((m_p, Z_p, (w @ V[a:a + P]) / Z_p))
+                M = max(m for m, _, _ in parts)
+                c = np.array([Z * np.exp(m - M) for m, Z, _ in parts])
+                o = np.stack([o for _, _, o in parts])
+                out[i, h] = (c @ o) / c.sum()
+    return out
+
+
+def decode_two_level(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                     block_tables: np.ndarray, context_lens: np.ndarray, scale, dtype: str,
+                     prefix_len: int, seqs: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Same result as :func:`decode`, with the shared prefix taken separately.
+
+    When every table starts with the same blocks (the book's §6: one copy of
+    a shared prompt referenced by many requests), positions [0, prefix_len)
+    can be attended through one table for all sequences and the rest through
+    each sequence's own. Each part keeps (max, exp-sum, normalised output) over
+    its positions below the sequence's length, and the two are merged with the
+    exp(m - M) rescale of :func:`decode_partitioned`.
+    """
+    B, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    G = Hq // Hkv
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    sc = float(np.float32(scale))
+    shared_row = block_tables[0]
+    out = np.zeros((len(seqs), Hq, D), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        L = int(context_lens[s])
+        if L == 0:
+            continue
+        lp = min(L, int(prefix_len))
+        for g in range(Hkv):
+            Kp = gather_positions(key_cache, shared_row, lp, g, dtype)
+            Vp = gather_positions(value_cache, shared_row, lp, g, dtype)
+            K = gather_positions(key_cache, block_tables[s], L, g, dtype)[lp:]
+            V = gather_positions(value_cache, block_tables[s], L, g, dtype)[lp:]
+            for h in range(g * G, (g + 1) * G):
+                qv = to_float64(q[s, h], dtype)
+                parts = []
+                for Kx, Vx in ((Kp, Vp), (K, V)):
+                    if len(Kx) == 0:
+                        continue
+                    logits = sc * (Kx @ qv)
+                    m_p = logits.max()
+                    w = np.exp(logits - m_p)
+                    parts.append((m_p, w.sum(), (w @ Vx) / w.sum()))
                 M = max(m for m, _, _ in parts)
                 c = np.array([Z * np.exp(m - M) for m, Z, _ in parts])
                 o = np.stack([o for _, _, o in parts])

@@ -156,6 +156,12 @@ int decode_impl(const void* q, const void* key_cache, const void* value_cache, b
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.len_cap = max_context_len;
+  a.tok_offset = 0;
+  a.slot_base = 0;
+  a.always_combine = 0;
+  a.prefix_len = 0;
+  a.prefix_chunks = 0;
+  a.prefix_row_tiles = 0;
   if (split) {
     const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
     const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, parts);
@@ -167,16 +173,41 @@ int decode_impl(const void* q, const void* key_cache, const void* value_cache, b
     a.ws_o = (float*)(ws + lay.o_off);
     a.part_tokens = P;
     a.num_parts = (int32_t)parts;
+    a.part_stride = (int32_t)parts;
     // Few (sequence, kv head) pairs: order the grid sequence by sequence.
     a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
   } else {
     a.part_tokens = max_context_len > 0 ? max_context_len : 1;
     a.num_parts = 1;
+    a.part_stride = 1;
     a.seq_major = 0;
   }
   const hipError_t e =
       pa::launch_decode(a, dtype, fp8_cache, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Partition plan of a cascade call: the suffix positions [prefix_len,
+// max_context_len) are split like an ordinary call over that range.
+struct CascadePlan {
+  int32_t prefix_len, suffix_max, part_tokens, num_parts, chunks, slots;
+};
+
+CascadePlan cascade_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                         int32_t max_context_len, int32_t shared_prefix_blocks,
+                         int32_t partition_size, int cus) {
+  CascadePlan c;
+  c.prefix_len = shared_prefix_blocks * block_size;
+  c.suffix_max = max_context_len > c.prefix_len ? max_context_len - c.prefix_len : 0;
+  int P = partition_size;
+  if (P == 0) P = auto_partition(num_seqs, num_kv_heads, c.suffix_max, cus);
+  if (P < 0) P = (int32_t)((c.suffix_max + 31) / 32 * 32);   // one partition
+  if (P <= 0) P = 32;                                           // no suffix at all
+  c.part_tokens = P;
+  c.num_parts = c.suffix_max > 0 ? (int32_t)ceil_div(c.suffix_max, P) : 1;
+  c.chunks = (int32_t)ceil_div(c.prefix_len, pa::kPrefixChunk);
+  c.slots = c.chunks + c.num_parts;
+  return c;
 }
 
 }  // namespace
@@ -281,6 +312,105 @@ int pa_decode_fp8(const void* q, const void* key_cache, const void* value_cache,
                      context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_size,
                      block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
                      dtype, workspace, workspace_size, stream);
+}
+
+
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t head_size, int32_t block_size,
+                                        int32_t max_context_len, int32_t shared_prefix_blocks,
+                                        int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads < 0 || head_size < 0 || block_size < 1 ||
+      max_context_len < 0 || shared_prefix_blocks < 0)
+    return 0;
+  if (shared_prefix_blocks == 0)
+    return pa_decode_workspace_size(num_seqs, num_q_heads, head_size, max_context_len,
+                                    partition_size);
+  const int64_t prefix_len = (int64_t)shared_prefix_blocks * block_size;
+  if (prefix_len > INT32_MAX) return 0;
+  const int64_t suffix_max = max_context_len > prefix_len ? max_context_len - prefix_len : 0;
+  const int64_t P = partition_size > 0 ? partition_size : kAutoMinPartition;
+  const int64_t parts = (partition_size < 0 || suffix_max == 0) ? 1 : ceil_div(suffix_max, P);
+  const int64_t slots = ceil_div(prefix_len, pa::kPrefixChunk) + parts;
+  return split_layout(num_seqs, num_q_heads, head_size, slots).total;
+}
+
+int pa_decode_cascade(const void* q, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_size, int32_t block_size, int64_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t shared_prefix_blocks, int32_t partition_size, int32_t dtype,
+                      void* workspace, size_t workspace_size, void* stream) {
+  if (shared_prefix_blocks < 0 || shared_prefix_blocks > max_blocks_per_seq) return PA_ERR_SHAPE;
+  if (shared_prefix_blocks == 0)
+    return decode_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_tables, context_lens,
+                       scale, out, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
+                       workspace, workspace_size, stream);
+  // Same validation as pa_decode (run with a single pass, which enqueues nothing
+  // when it fails and is not used when it passes).
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+
+  int cus = device_cu_count();
+  if (cus <= 0) cus = kFallbackCUs;
+  const CascadePlan c = cascade_plan(num_seqs, num_kv_heads, block_size, max_context_len,
+                                     shared_prefix_blocks, partition_size, cus);
+  const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, c.slots);
+  if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)num_seqs * group;
+
+  pa::DecodeParams a;
+  a.q = (const uint16_t*)q;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.bt = block_tables;
+  a.lens = context_lens;
+  a.out = (uint16_t*)out;
+  char* ws = (char*)workspace;
+  a.ws_m = (float*)(ws + lay.m_off);
+  a.ws_l = (float*)(ws + lay.l_off);
+  a.ws_o = (float*)(ws + lay.o_off);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.v_scale = 1.f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.log2_block_size = ilog2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.len_cap = max_context_len;
+  a.part_tokens = c.part_tokens;
+  a.num_parts = c.num_parts;
+  a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
+  a.tok_offset = c.prefix_len;
+  a.slot_base = c.chunks;
+  a.part_stride = c.slots;
+  a.always_combine = 0;     // one-partition suffixes fold the prefix in the partition kernel
+  a.prefix_len = c.prefix_len;
+  a.prefix_chunks = c.chunks;
+  a.prefix_row_tiles = (int32_t)((rows + 63) / 64);
+  const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // extern "C"

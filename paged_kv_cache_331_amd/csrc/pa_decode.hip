@@ -34,6 +34,27 @@
 namespace pa {
 namespace {
 
+// Folds the shared-prefix partials (slots 0 .. nslots-1 of row oh, written by
+// the cascade's prefix kernel) into a running (M, num, den) of one output
+// element d: the split-K rescale by 2^(m - M).
+__device__ __forceinline__ void fold_prefix(const DecodeParams& a, int64_t oh, int d, int D,
+                                            int nslots, float& M, float& num, float& den) {
+  const float* pm = a.ws_m + oh * a.part_stride;
+  const float* pl = a.ws_l + oh * a.part_stride;
+  const float* po = a.ws_o + oh * a.part_stride * D + d;
+  float Mn = M;
+  for (int c = 0; c < nslots; ++c) Mn = fmaxf(Mn, pm[c]);
+  const float r = fast_exp2(M - Mn);
+  num *= r;
+  den *= r;
+  for (int c = 0; c < nslots; ++c) {
+    const float w = fast_exp2(pm[c] - Mn);
+    num = fmaf(w, po[(int64_t)c * D], num);
+    den = fmaf(w, pl[c], den);
+  }
+  M = Mn;
+}
+
 constexpr float kEmptyMax = -1.0e30f;  // running max before any token: finite, so
                                        // exp2(m_old - m_new) never sees inf - inf
 constexpr int kTile = 16;                  // tokens per wave iteration
@@ -76,12 +97,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
 
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int start = p * a.part_tokens;
+  const int start = a.tok_offset + p * a.part_tokens;
   const int tid = threadIdx.x;
   if (start >= L) {
-    if (p == 0) {  // empty sequence: the output stays zero
+    if (p == 0 && !a.always_combine) {
+      // No token past the offset: an empty sequence stays zero; in a cascade a
+      // sequence that ends inside the shared prefix is the prefix partials alone.
       uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
-      for (int i = tid; i < G * D; i += NT) o[i] = 0;
+      const bool pfx = a.slot_base > 0 && L > 0;
+      for (int i = tid; i < G * D; i += NT) {
+        float M = kEmptyMax, num = 0.f, den = 0.f;
+        if (pfx) {
+          const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + i / D;
+          fold_prefix(a, oh, i % D, D, a.slot_base, M, num, den);
+        }
+        o[i] = pfx ? S::from_float(num / den) : (uint16_t)0;
+      }
     }
     return;
   }
@@ -226,7 +257,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   __syncthreads();
 
   // Merge the waves: rescale each wave's partial sums to the common max.
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;  // partitions holding tokens
+  // partitions holding tokens
+  const int np = (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens;
+  const bool finish = np == 1 && !a.always_combine;
   for (int i = tid; i < G * D; i += NT) {
     const int h = i / D;
     const int d = i % D;
@@ -242,10 +275,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
     }
     num *= a.v_scale;                                   // 1 unless the cache is FP8
     const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
-    if (np == 1) {
+    if (finish) {
+      if (a.slot_base > 0) fold_prefix(a, oh, d, D, a.slot_base, M, num, den);
       a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
     } else {
-      const int64_t pi = oh * a.num_parts + p;
+      const int64_t pi = oh * a.part_stride + a.slot_base + p;
       a.ws_o[pi * D + d] = num;
       if (d == 0) {
         a.ws_m[pi] = M;
@@ -277,12 +311,18 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int tid = threadIdx.x;
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;
-
   const int64_t oh = (int64_t)s * a.num_q_heads + h;
-  const float* pm = a.ws_m + oh * a.num_parts;
-  const float* pl = a.ws_l + oh * a.num_parts;
+  if (L == 0) {                          // a cascade leaves empty sequences to this kernel
+    if (a.always_combine)
+      for (int d = tid; d < D; d += NT) a.out[oh * D + d] = 0;
+    return;
+  }
+  const int own = L > a.tok_offset ? (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens : 0;
+  const int np = a.slot_base + own;      // partial slots holding this sequence's tokens
+  if (own <= 1 && !a.always_combine) return;   // finished by the partition kernel
+
+  const float* pm = a.ws_m + oh * a.part_stride;
+  const float* pl = a.ws_l + oh * a.part_stride;
 
   // M = max over the partitions' running maxima.
   float M = kEmptyMax;
@@ -297,7 +337,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
 
   const int c = tid % CH;
   const int grp = tid / CH;
-  const float4* po = reinterpret_cast<const float4*>(a.ws_o + oh * a.num_parts * D) + c;
+  const float4* po = reinterpret_cast<const float4*>(a.ws_o + oh * a.part_stride * D) + c;
   float den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
@@ -338,7 +378,7 @@ hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G>), dim3((uint32_t)nwg),
                      dim3(kDecodeWaves * 64), 0, st, a);
-  if (a.num_parts == 1) return hipGetLastError();
+  if (a.num_parts == 1 && !a.always_combine) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t nr = (uint64_t)a.num_q_heads * a.num_seqs;

@@ -31,6 +31,16 @@ struct DecodeParams {
                             // at least max_context_len when there is no split
   int32_t num_parts;        // partitions per sequence in the grid (1: no split, no workspace)
   int32_t seq_major;        // grid order: 1 = sequence index slowest, 0 = partition slowest
+  int32_t tok_offset;       // first position the partitions cover (a multiple of block_size;
+                            // the shared-prefix length in a cascade, else 0)
+  int32_t slot_base;        // partial slots before the partitions' own (prefix chunks)
+  int32_t part_stride;      // partial slots per (sequence, query head) in the workspace
+  int32_t always_combine;   // 1: every sequence goes through the combine kernel
+  // Cascade only: attention of every (sequence, query head) over the shared
+  // prefix, positions [0, prefix_len) through block_tables row 0.
+  int32_t prefix_len;       // tokens (a multiple of block_size)
+  int32_t prefix_chunks;    // prefix key chunks = partial slots 0 .. prefix_chunks-1
+  int32_t prefix_row_tiles; // 64-row tiles of the num_seqs * group query rows
   int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
 };
 
@@ -39,10 +49,18 @@ struct DecodeParams {
 constexpr int kDecodeWaves = 4;
 constexpr int kReduceThreads = 256;
 
+// Keys of the shared prefix one cascade work-group covers.
+constexpr int kPrefixChunk = 128;
+
 // One decode step: the partition kernel, then (num_parts > 1) the combine.
 // dtype: q / out type (0 fp16, 1 bf16); fp8_cache: the caches hold E4M3 codes.
 hipError_t launch_decode(const DecodeParams& a, int dtype, bool fp8_cache, int head_size,
                          int group, hipStream_t stream);
+
+// Cascade decode: the prefix kernel (MFMA), the partition kernel over the
+// positions past the prefix, then the combine of both kinds of partials.
+hipError_t launch_cascade(const DecodeParams& a, int dtype, int head_size, int group,
+                          hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq,
                                const int32_t* lens, int32_t num_seqs, int32_t block_size,

@@ -38,6 +38,10 @@ SIGNATURES = {
                                  _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_cache_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
                                           _i32, _f32, _f32, _vp]),
+    "pa_decode_cascade_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                         _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz,
                                      _vp]),
@@ -211,4 +215,41 @@ def decode_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                               int(max_context_len), int(partition_size), dtype_code(q.dtype),
                               ws_ptr, ws_len, _stream(stream))
     _check("pa_decode_fp8", st)
+    return out
+
+
+def decode_cascade_workspace_size(num_seqs: int, num_q_heads: int, head_size: int,
+                                  block_size: int, max_context_len: int,
+                                  shared_prefix_blocks: int, partition_size: int = 0) -> int:
+    return int(load().pa_decode_cascade_workspace_size(num_seqs, num_q_heads, head_size,
+                                                       block_size, max_context_len,
+                                                       shared_prefix_blocks, partition_size))
+
+
+def decode_cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                   max_context_len: int, shared_prefix_blocks: int,
+                   out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode step whose tables share their first ``shared_prefix_blocks`` entries."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_cascade_workspace_size(B, Hq, D, bs, max_context_len, shared_prefix_blocks,
+                                         partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().pa_decode_cascade(_dev(q, "q"), _dev(key_cache, "key_cache"),
+                                  _dev(value_cache, "value_cache"),
+                                  _dev(block_tables, "block_tables"),
+                                  _dev(context_lens, "context_lens"), float(scale),
+                                  _dev(out, "out"), B, Hq, Hkv, D, bs, NB, MB,
+                                  int(max_context_len), int(shared_prefix_blocks),
+                                  int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
+                                  _stream(stream))
+    _check("pa_decode_cascade", st)
     return out

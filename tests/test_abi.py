@@ -29,7 +29,8 @@ def test_header_declares_expected_api():
     assert _declared() == sorted(["pa_abi_version", "pa_status_string", "pa_decode_slot_mapping",
                                   "pa_cache_write", "pa_decode_workspace_size",
                                   "pa_decode_partition_size", "pa_decode", "pa_cache_write_fp8",
-                                  "pa_decode_fp8"])
+                                  "pa_decode_fp8", "pa_decode_cascade",
+                                  "pa_decode_cascade_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -214,3 +215,34 @@ def test_cache_write_fp8_validation(lib, kw, code):
 def test_fp8_zero_work_is_ok(lib):
     assert _write_fp8(T=0, k=None, v=None, kc=None, vc=None, slots=None) == 0
     assert _decode_fp8(B=0, q=None, out=None) == 0
+
+
+def test_cascade_workspace_arithmetic(lib):
+    ws = pa.load().pa_decode_cascade_workspace_size
+    al = lambda x: (x + 255) // 256 * 256
+    # 128 sequences x 32 heads; prefix 32 blocks of 32 = 1024 tokens -> 4 chunks of 256;
+    # suffix up to 1536 - 1024 = 512 tokens in partitions of 256 -> 2; 6 slots
+    n = 128 * 32 * 6
+    assert ws(128, 32, 128, 32, 1536, 32, 256) == 2 * al(4 * n) + al(4 * n * 128)
+    assert ws(128, 32, 128, 32, 1536, 0, 256) == pa.load().pa_decode_workspace_size(
+        128, 32, 128, 1536, 256)
+    assert ws(-1, 32, 128, 32, 1536, 32, 256) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pfx=-1), -2),
+    (dict(pfx=5), -2),                   # beyond max_blocks_per_seq
+    (dict(dtype=2), -3),
+    (dict(D=96), -4),
+    (dict(ws=None, wss=0), -5),
+    (dict(q=None), -1),
+])
+def test_cascade_validation(lib, kw, code):
+    a = dict(q=16, kc=16, vc=16, bt=16, lens=16, scale=0.125, out=16, B=2, Hq=4, Hkv=4, D=128,
+             bs=16, NB=10, MB=4, maxlen=64, pfx=2, P=-1, dtype=F, ws=None, wss=0, stream=None)
+    a.update(kw)
+    st = pa.load().pa_decode_cascade(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"],
+                                     a["out"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                     a["MB"], a["maxlen"], a["pfx"], a["P"], a["dtype"], a["ws"],
+                                     a["wss"], a["stream"])
+    assert st == code

@@ -447,3 +447,23 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     decode_fn = fn if fn is not None else opa.decode
     failed = [p.__name__ for p in ALL_DECODE_PINS if not p(decode_fn)]
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+
+@pytest.mark.parametrize("prefix_blocks", [1, 2, 3])
+def test_two_level_prefix_identity(prefix_blocks):
+    """The shared-prefix reformulation equals the plain definition, including
+    sequences shorter than the prefix and an empty one."""
+    spec = wl.WorkloadSpec(name="pfx", num_seqs=5, num_q_heads=4, num_kv_heads=2, head_size=16,
+                           block_size=16, dtype="fp16", lengths="uniform", len_lo=1, len_hi=40,
+                           shared_prefix_blocks=prefix_blocks, seed_index=77)
+    b = wl.make_batch(spec)
+    pfx = prefix_blocks * 16
+    lens = b.context_lens.copy()
+    lens[0], lens[1], lens[2] = 0, max(1, pfx // 2), pfx
+    assert np.all(b.block_tables[:, :prefix_blocks] == b.block_tables[0, :prefix_blocks])
+    ref = oracle.decode(b.q, b.key_cache, b.value_cache, b.block_tables, lens, b.scale, b.dtype)
+    got = oracle.decode_two_level(b.q, b.key_cache, b.value_cache, b.block_tables, lens, b.scale,
+                                  b.dtype, pfx)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+    assert np.all(got[0] == 0)

@@ -49,7 +49,8 @@ import numpy as np
 __all__ = [
     "to_float64", "physical_slot", "slot_mapping", "cache_write",
     "gather_positions", "decode", "decode_one", "attention_weights",
-    "decode_partitioned", "decode_two_level", "blocks_needed",
+    "decode_partitioned", "decode_two_level", "prefill", "prefill_slot_mapping",
+    "blocks_needed",
 ]
 
 
@@ -278,4 +279,57 @@ def decode_two_level(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarr
                 c = np.array([Z * np.exp(m - M) for m, Z, _ in parts])
                 o = np.stack([o for _, _, o in parts])
                 out[i, h] = (c @ o) / c.sum()
+    return out
+
+
+def prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+            block_tables: np.ndarray, context_lens: np.ndarray, query_start: np.ndarray,
+            scale, dtype: str) -> np.ndarray:
+    """Causal attention of each sequence's new tokens over its paged cache.
+
+    The book's §4 prefill phase: the N new tokens' K and V are first written
+    into the blocks the table points to, then attention runs over them. With
+    chunked prompts a sequence may already hold earlier tokens, so sequence s
+    has ``n = query_start[s+1] - query_start[s]`` new tokens (rows
+    ``query_start[s] .. query_start[s+1]-1`` of ``q``) at positions
+    ``L - n .. L - 1`` of its ``L = context_lens[s]`` cached positions. The
+    new token at position ``p`` attends to positions ``0 .. p``.
+    Returns float64 ``[num_tokens, Hq, D]``.
+    """
+    T, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    qs = np.asarray(query_start, dtype=np.int64)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        a, b = int(qs[s]), int(qs[s + 1])
+        n = b - a
+        if n == 0:
+            continue
+        assert n <= L, "more new tokens than cached positions"
+        for g in range(Hkv):
+            K = gather_positions(key_cache, block_tables[s], L, g, dtype)
+            V = gather_positions(value_cache, block_tables[s], L, g, dtype)
+            for i in range(n):
+                pos = L - n + i
+                for h in range(g * G, (g + 1) * G):
+                    out[a + i, h], _ = _softmax_attend(to_float64(q[a + i, h], dtype),
+                                                       K[:pos + 1], V[:pos + 1], sc)
+    return out
+
+
+def prefill_slot_mapping(block_tables: np.ndarray, context_lens: np.ndarray,
+                         query_start: np.ndarray, block_size: int) -> np.ndarray:
+    """Slot of every new token: row ``query_start[s] + i`` holds position
+    ``L - n + i`` of sequence s (the book's §4 prefill writes the new tokens'
+    K/V in order into the blocks the table points to)."""
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.empty(int(qs[-1]), dtype=np.int32)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        n = int(qs[s + 1] - qs[s])
+        for i in range(n):
+            out[qs[s] + i] = physical_slot(block_tables[s], L - n + i, block_size)
     return out

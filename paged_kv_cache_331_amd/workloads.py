@@ -37,6 +37,7 @@ SEED_ROOT = 331
 _CHUNK = 1 << 22
 # Seed-stream ids for the independent draws of one batch.
 _STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_KNEW, _STREAM_VNEW = 1, 2, 3, 4, 5
+_STREAM_PREFILL_POOL = 6
 
 DTYPES = ("fp16", "bf16")
 
@@ -122,6 +123,88 @@ CONFIGS = {
 }
 CONFIG_ORDER = ("tiny_write", "llama2_7b_mha", "gqa_8b", "long_context_splitk",
                 "prefix_shared_write")
+
+
+@dataclass(frozen=True)
+class PrefillSpec:
+    """A prefill batch: each sequence holds ``ctx`` cached tokens and receives
+    ``new`` prompt tokens (the book's §4 prefill phase; ctx = 0 is a whole
+    prompt, ctx > 0 a later chunk of a chunked prompt)."""
+
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    dtype: str
+    ctx_lo: int
+    ctx_hi: int
+    new_lo: int
+    new_hi: int
+    seed_index: int
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+PREFILL_CONFIGS = {
+    # Llama-2-7B-shaped whole prompts of 512..2048 tokens.
+    "llama2_7b_prefill": PrefillSpec(
+        name="llama2_7b_prefill", num_seqs=4, num_q_heads=32, num_kv_heads=32, head_size=128,
+        block_size=16, dtype="fp16", ctx_lo=0, ctx_hi=0, new_lo=512, new_hi=2048, seed_index=8),
+    # GQA 8B-shaped chunked prefill: 0..2048 cached tokens plus a 64..512-token chunk.
+    "gqa_8b_chunked_prefill": PrefillSpec(
+        name="gqa_8b_chunked_prefill", num_seqs=16, num_q_heads=32, num_kv_heads=8,
+        head_size=128, block_size=16, dtype="bf16", ctx_lo=0, ctx_hi=2048, new_lo=64, new_hi=512,
+        seed_index=9),
+}
+PREFILL_ORDER = ("llama2_7b_prefill", "gqa_8b_chunked_prefill")
+
+
+@dataclass
+class PrefillBatch:
+    """Host arrays of one prefill batch. ``k_new`` / ``v_new`` are the new
+    tokens' K/V, to be written before attention; the pool already holds the
+    earlier context."""
+
+    spec: PrefillSpec
+    q: np.ndarray              # uint16 [T, Hq, D]
+    key_cache: np.ndarray      # uint16 [NB, bs, Hkv, D]
+    value_cache: np.ndarray
+    block_tables: np.ndarray   # int32 [B, MB]
+    context_lens: np.ndarray   # int32 [B], cached tokens after the new ones are written
+    query_start: np.ndarray    # int32 [B + 1]
+    k_new: np.ndarray          # uint16 [T, Hkv, D]
+    v_new: np.ndarray
+    scale: np.float32
+    used_blocks: np.ndarray
+
+    @property
+    def dtype(self) -> str:
+        return self.spec.dtype
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.key_cache.shape[0])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def max_query_len(self) -> int:
+        n = np.diff(self.query_start)
+        return int(n.max()) if n.size else 0
 FP8_ORDER = ("llama2_7b_mha_fp8", "gqa_8b_fp8")
 
 
@@ -341,3 +424,35 @@ def poison_unused_blocks(batch: Batch) -> None:
     nb = nan_bits(batch.cache_dtype)
     batch.key_cache[mask] = nb
     batch.value_cache[mask] = nb
+
+
+def make_prefill_batch(spec: PrefillSpec, *, ctx: Optional[Sequence[int]] = None,
+                       new: Optional[Sequence[int]] = None,
+                       num_seqs: Optional[int] = None) -> PrefillBatch:
+    """Draw a prefill batch: ctx and new-token counts (uniform, inclusive) from
+    ``default_rng([331, seed_index])``, tables over a shuffled pool of the
+    blocks used plus 10%, then q / pool / new k, v from their own streams."""
+    key = [SEED_ROOT, spec.seed_index]
+    rng = np.random.default_rng(key)
+    B = num_seqs if num_seqs is not None else spec.num_seqs
+    c = np.asarray(ctx, np.int64) if ctx is not None else \
+        rng.integers(spec.ctx_lo, spec.ctx_hi, size=B, endpoint=True)
+    n = np.asarray(new, np.int64) if new is not None else \
+        rng.integers(spec.new_lo, spec.new_hi, size=B, endpoint=True)
+    lens = (c + n).astype(np.int32)
+    dec = WorkloadSpec(name=spec.name, num_seqs=len(lens), num_q_heads=spec.num_q_heads,
+                       num_kv_heads=spec.num_kv_heads, head_size=spec.head_size,
+                       block_size=spec.block_size, dtype=spec.dtype, lengths="uniform",
+                       len_lo=1, len_hi=max(1, int(lens.max()) if lens.size else 1),
+                       seed_index=spec.seed_index)
+    b = make_batch(dec, lengths=lens, seed=key + [_STREAM_PREFILL_POOL])
+    T = int(n.sum())
+    Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_size
+    q = fill_normal((T, Hq, D), spec.dtype, key + [_STREAM_Q])
+    k_new = fill_normal((T, Hkv, D), spec.dtype, key + [_STREAM_KNEW])
+    v_new = fill_normal((T, Hkv, D), spec.dtype, key + [_STREAM_VNEW])
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    return PrefillBatch(spec=spec, q=q, key_cache=b.key_cache, value_cache=b.value_cache,
+                        block_tables=b.block_tables, context_lens=lens, query_start=qs,
+                        k_new=k_new, v_new=v_new, scale=np.float32(1.0 / math.sqrt(D)),
+                        used_blocks=b.used_blocks)

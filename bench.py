@@ -212,6 +212,122 @@ def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 20) -> dict:
     return {"bytes": nbytes, "GBs": 2 * nbytes / t / 1e9, "ms": t * 1e3}
 
 
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, AMD's published figure
+PREFILL_METRIC = "prefill tokens/s + TFLOP/s (% of MI355X dense fp16/bf16 MFMA peak), 1 GPU"
+
+
+def prefill_flops(spec, context_lens: np.ndarray, query_start: np.ndarray) -> int:
+    """Causal attention FLOPs: 4 * head_size per (new token, query head, visible position)."""
+    total = 0
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        n = int(query_start[s + 1] - query_start[s])
+        # positions L-n .. L-1 see L-n+1 .. L keys
+        total += n * (L - n) + n * (n + 1) // 2
+    return 4 * spec.head_size * spec.num_q_heads * total
+
+
+def prefill_cpu_baseline(batch, budget_s: float) -> dict:
+    """The fp64 oracle's prefill arithmetic row by row (one new token, all its
+    heads, at its own length) until ``budget_s`` of single-thread CPU time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    qs = batch.query_start
+    rows = [(s, i) for s in range(batch.num_seqs) for i in range(int(qs[s + 1] - qs[s]))]
+    order = np.random.default_rng(0).permutation(len(rows))
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        while True:
+            s, i = rows[order[done % len(rows)]]
+            n = int(qs[s + 1] - qs[s])
+            L1 = np.array([int(batch.context_lens[s]) - n + i + 1], np.int32)
+            oracle.decode(batch.q[qs[s] + i][None], batch.key_cache, batch.value_cache,
+                          batch.block_tables[s:s + 1], L1, batch.scale, batch.dtype)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, one thread: {done} new-token rows (all query heads "
+                       f"of a token at its own causal length), drawn at random from the "
+                       f"{len(rows)}-token batch, in {dt:.1f} s")}
+
+
+def run_prefill(args) -> int:
+    """One step = slots of the new tokens + their cache write + causal prefill."""
+    import torch
+    from paged_kv_cache_331_amd import pa, workloads as wl
+    spec = wl.PREFILL_CONFIGS[args.workload]
+    print(f"# generating {spec.name}", file=sys.stderr, flush=True)
+    b = wl.make_prefill_batch(spec)
+    tdt = torch.float16 if spec.dtype == "fp16" else torch.bfloat16
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).cuda()
+    q, kc, vc, k_new, v_new = up(b.q), up(b.key_cache), up(b.value_cache), up(b.k_new), up(b.v_new)
+    bt = torch.from_numpy(b.block_tables).cuda()
+    lens = torch.from_numpy(b.context_lens).cuda()
+    qs = torch.from_numpy(b.query_start).cuda()
+    out = torch.empty_like(q)
+    slots = torch.empty(b.num_tokens, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    T, mq, ml = b.num_tokens, b.max_query_len, b.max_context_len
+
+    def step(ev0=None, ev1=None):
+        pa.prefill_slot_mapping(bt, lens, qs, T, mq, spec.block_size, ml, out=slots, stream=stream)
+        pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        pa.prefill(q, kc, vc, bt, lens, qs, float(b.scale), mq, ml, out=out, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    pf_ms = float(np.mean(ms))
+    ms_per_step = wall * 1e3 / args.steps
+    flops = prefill_flops(spec, b.context_lens, b.query_start)
+    achieved = flops / (pf_ms * 1e-3) / 1e12
+    base = prefill_cpu_baseline(b, args.cpu_budget) if args.cpu_budget > 0 else None
+    line = {
+        "metric": PREFILL_METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block tables)",
+        "config": {"workload": spec.name, "num_seqs": b.num_seqs, "new_tokens": T,
+                   "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_size": spec.head_size, "block_size": spec.block_size,
+                   "cached_before": f"uniform [{spec.ctx_lo}, {spec.ctx_hi}]",
+                   "new_per_seq": f"uniform [{spec.new_lo}, {spec.new_hi}]",
+                   "step": "prefill slot mapping + cache write + causal prefill",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill (events around the call on its stream)",
+                     "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "prefill_ms_mean": pf_ms, "prefill_ms_min": float(np.min(ms))},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +368,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_probe": copy_bandwidth()}), flush=True)
         return 0
     pa.load()          # the HIP library must be built; there is no fallback
+    if args.workload in wl.PREFILL_CONFIGS:
+        return run_prefill(args)
     spec = wl.CONFIGS[args.workload]
     print(f"# generating {spec.name}", file=sys.stderr, flush=True)
     batch = wl.make_batch(spec)

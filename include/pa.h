@@ -298,6 +298,62 @@ PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* v
                              int32_t partition_size, int32_t dtype, void* workspace,
                              size_t workspace_size, void* stream);
 
+/*
+ * Prefill batches ("01. PagedAttention 详解" §4, prefill phase: a prompt's N
+ * tokens get their K/V written into the blocks the table points to, then
+ * attention runs over them). Sequence s holds L = context_lens[s] positions
+ * once its new tokens are written; its n = query_start[s+1] - query_start[s]
+ * new tokens are rows query_start[s] .. query_start[s+1]-1 of q / out /
+ * slot_mapping, at positions L - n .. L - 1 (a whole prompt when n == L, a
+ * later chunk of one when n < L).
+ * query_start : int32 [num_seqs + 1] (device), non-decreasing, from 0 to
+ *               num_tokens; rows outside [0, num_tokens) are never touched and
+ *               n is capped at min(L, max_query_len).
+ * max_query_len : host-known upper bound of n (sizes the grid).
+ */
+
+/*
+ * pa_prefill_slot_mapping -- slot of every new token:
+ *   slot_mapping[query_start[s] + i] = block_tables[s][p / block_size] * block_size
+ *                                      + p % block_size,   p = L - n + i.
+ * The result feeds pa_cache_write with num_tokens tokens. Exact integer
+ * arithmetic. Errors: PA_ERR_SHAPE (negative sizes, max_context_len beyond
+ * the table), PA_ERR_UNSUPPORTED (num_seqs > 65535), PA_ERR_NULL.
+ * num_seqs == 0 or num_tokens == 0 enqueues nothing and returns PA_OK.
+ */
+PA_API int pa_prefill_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, const int32_t* query_start,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                   int32_t block_size, int32_t max_context_len,
+                                   int32_t* slot_mapping, void* stream);
+
+/*
+ * pa_prefill -- causal paged attention of the new tokens.
+ *
+ * For each new token (row t of sequence s at position p) and query head h:
+ *   out[t, h, :] = sum_{u <= p} softmax_u(scale * q[t,h,:] . K_u) * V_u
+ * with K_u / V_u the rows of kv head h / (num_q_heads / num_kv_heads) at
+ * position u of sequence s, reached through block_tables[s]. The new tokens'
+ * K/V must already be in the cache (pa_prefill_slot_mapping +
+ * pa_cache_write). The products run on the matrix cores in fp32
+ * accumulation; the softmax weights enter the P.V product rounded to the
+ * query's 2-byte type.
+ * q, out : [num_tokens, num_q_heads, head_size] of dtype (device)
+ * caches : [num_blocks, block_size, num_kv_heads, head_size] of dtype
+ * Only table entries of positions < L are read; block ids outside
+ * [0, num_blocks) read as zeros. No workspace is needed.
+ * Errors: as pa_decode (dtype, shapes, head size 64 / 128, block size
+ * 16 / 32, group 1 / 2 / 4 / 8, alignment, NULL, HIP). num_seqs, num_tokens
+ * or max_query_len == 0 returns PA_OK.
+ */
+PA_API int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start, float scale, void* out, int32_t num_seqs,
+                      int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -413,4 +413,80 @@ int pa_decode_cascade(const void* q, const void* key_cache, const void* value_ca
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+
+int pa_prefill_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                            int32_t block_size, int32_t max_context_len, int32_t* slot_mapping,
+                            void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_blocks_per_seq < 1 ||
+      block_size < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!block_tables || !context_lens || !query_start || !slot_mapping) return PA_ERR_NULL;
+  pa::PrefillParams p = {};
+  p.bt = block_tables;
+  p.lens = context_lens;
+  p.query_start = query_start;
+  p.slots = slot_mapping;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.max_query_len = max_query_len;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.len_cap = max_context_len;
+  const hipError_t e = pa::launch_prefill_slots(p, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, float scale, void* out, int32_t num_seqs,
+               int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_size, int32_t block_size, int64_t num_blocks,
+               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype, void* stream) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 0 ||
+      max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start ||
+      !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+  pa::PrefillParams p = {};
+  p.q = (const uint16_t*)q;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.bt = block_tables;
+  p.lens = context_lens;
+  p.query_start = query_start;
+  p.out = (uint16_t*)out;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.max_query_len = max_query_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.log2_block_size = ilog2_exact(block_size);
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.len_cap = max_context_len;
+  p.num_blocks = num_blocks;
+  const hipError_t e = pa::launch_prefill(p, dtype, head_size, group, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -49,6 +49,27 @@ struct DecodeParams {
 constexpr int kDecodeWaves = 4;
 constexpr int kReduceThreads = 256;
 
+// Everything one prefill launch needs. Pointers are device pointers.
+struct PrefillParams {
+  const uint16_t* q;          // [num_tokens, Hq, D]
+  const void* kc;             // [NB, bs, Hkv, D]
+  const void* vc;
+  const int32_t* bt;          // [B, MB]
+  const int32_t* lens;        // [B], positions after the new tokens are written
+  const int32_t* query_start; // [B + 1], rows of each sequence's new tokens
+  uint16_t* out;              // [num_tokens, Hq, D]
+  int32_t* slots;             // [num_tokens] (slot kernel only)
+  float scale_log2;
+  int32_t num_seqs, num_tokens, max_query_len;
+  int32_t num_q_heads, num_kv_heads, block_size, log2_block_size;
+  int32_t max_blocks_per_seq, len_cap, num_tiles;
+  int64_t num_blocks;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group,
+                          hipStream_t stream);
+hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
+
 // Keys of the shared prefix one cascade work-group covers.
 constexpr int kPrefixChunk = 128;
 

@@ -1,0 +1,175 @@
+// Paged prefill for gfx950: the new tokens of each sequence (a whole prompt,
+// or a later chunk of one) attend causally to every cached position up to
+// their own, through the sequence's block table ("01. PagedAttention 详解"
+// §4, prefill phase: the N new tokens' K and V are written into the blocks
+// the table points to, then attention runs over them).
+//
+// Sequence s holds L = context_lens[s] positions after the write; its n new
+// tokens are rows query_start[s] .. query_start[s+1]-1 of q / out, at
+// positions L - n .. L - 1. The token at position p attends to 0 .. p.
+//
+// Work decomposition: one work-group per (kv head g, sequence s, tile of
+// 64 / G new tokens): its 64 query rows are those tokens' G query heads of kv
+// head g (so each K/V row staged serves G heads), on the matrix-core core of
+// pa_mq.h. The work-group walks positions 0 .. (its last token's position)
+// in chunks of 256 table entries staged in LDS; each row masks the keys past
+// its own position. Tiles with more keys (later in a sequence) are
+// dispatched first.
+#include "pa_launch.h"
+#include "pa_mq.h"
+
+namespace pa {
+namespace {
+
+constexpr int kSlotThreads = 256;
+constexpr int kTblChunk = 256;           // table entries staged per LDS pass
+
+// Clamped view of sequence s's new-token rows: [a, a + n).
+__device__ __forceinline__ void new_rows(const PrefillParams& p, int s, int L, int& a, int& n) {
+  const int T = p.num_tokens;
+  int q0 = p.query_start[s], q1 = p.query_start[s + 1];
+  q0 = q0 < 0 ? 0 : (q0 > T ? T : q0);
+  q1 = q1 < q0 ? q0 : (q1 > T ? T : q1);
+  a = q0;
+  n = min(q1 - q0, min(L, p.max_query_len));
+}
+
+__global__ __launch_bounds__(kSlotThreads) void prefill_slot_kernel(const PrefillParams p) {
+  const int s = blockIdx.y;
+  int L = p.lens[s];
+  L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+  int a, n;
+  new_rows(p, s, L, a, n);
+  const int i = blockIdx.x * kSlotThreads + threadIdx.x;
+  if (i >= n) return;
+  const int pos = L - n + i;
+  const int32_t* row = p.bt + (int64_t)s * p.max_blocks_per_seq;
+  p.slots[a + i] = row[pos / p.block_size] * p.block_size + pos % p.block_size;
+}
+
+template <class DT, int D, int G>
+__global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillParams p) {
+  using S = Storage<DT>;
+  constexpr int NT = kMqWaves * 64;
+  constexpr int TPW = kMqRowsPerWg / G;    // new tokens per work-group
+  static_assert(D == 64 || D == 128, "head size");
+  __shared__ int32_t s_tbl[kTblChunk];
+  __shared__ MqLds<D> lds;
+
+  const int Hkv = p.num_kv_heads;
+  int wg = blockIdx.x;
+  const int g = wg % Hkv;
+  wg /= Hkv;
+  const int s = wg % p.num_seqs;
+  const int qt = p.num_tiles - 1 - wg / p.num_seqs;   // the longest tiles first
+  int L = p.lens[s];
+  L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+  int a, n;
+  new_rows(p, s, L, a, n);
+  if (qt * TPW >= n) return;                           // uniform: no token in this tile
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 15;
+  const int grp = lane >> 4;
+  const int r = wave * kMqRowsPerWave + j;             // row of the work-group
+  const int ti = qt * TPW + r / G;                     // new token index in the sequence
+  const int h = g * G + r % G;
+  const bool row_ok = ti < n;
+  const int pos = L - n + ti;                          // its position
+  const int row_end = row_ok ? pos + 1 : 0;            // causal: keys 0 .. pos
+  const int kend = L - n + min(n, (qt + 1) * TPW);     // one past the tile's last position
+
+  u32x4_t qb[D / 32];
+  mq_load_q<D>(qb, p.q + ((int64_t)(a + (row_ok ? ti : 0)) * p.num_q_heads + h) * D, row_ok);
+  MqState<D> st;
+  st.init();
+
+  const int32_t* bt_row = p.bt + (int64_t)s * p.max_blocks_per_seq;
+  const int lbs = p.log2_block_size;
+  const int bs = p.block_size;
+  const int64_t tok_stride = (int64_t)Hkv * D;
+  const int chunk_tokens = kTblChunk * bs;
+  for (int c0 = 0; c0 < kend; c0 += chunk_tokens) {
+    const int c1 = min(kend, c0 + chunk_tokens);
+    const int b0 = c0 >> lbs;
+    const int nb = (c1 - c0 + bs - 1) >> lbs;
+    for (int i = tid; i < nb; i += NT) {
+      const int blk = bt_row[b0 + i];
+      s_tbl[i] = (uint64_t)(uint32_t)blk < (uint64_t)p.num_blocks ? blk : -1;
+    }
+    __syncthreads();
+    auto slot_of = [&](int t) -> int64_t {
+      const int blk = s_tbl[(t >> lbs) - b0];
+      return blk < 0 ? -1 : (int64_t)blk * bs + (t & (bs - 1));
+    };
+    mq_attend<DT, D>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
+                     static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
+                     p.scale_log2, slot_of);   // ends with a barrier: s_tbl is free again
+  }
+
+  const float lsum = mq_sum_over_groups(st.lsum);
+  if (!row_ok) return;
+  const float inv = 1.f / lsum;
+  uint16_t* o = p.out + ((int64_t)(a + ti) * p.num_q_heads + h) * D + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    uint2 w;
+    w.x = (uint32_t)S::from_float(st.acc[dt][0] * inv) |
+          ((uint32_t)S::from_float(st.acc[dt][1] * inv) << 16);
+    w.y = (uint32_t)S::from_float(st.acc[dt][2] * inv) |
+          ((uint32_t)S::from_float(st.acc[dt][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(o + 16 * dt) = w;
+  }
+}
+
+template <class DT, int D, int G>
+hipError_t launch_pf(const PrefillParams& p, hipStream_t st) {
+  constexpr int TPW = kMqRowsPerWg / G;
+  PrefillParams q = p;
+  q.num_tiles = (p.max_query_len + TPW - 1) / TPW;
+  const uint64_t nwg = (uint64_t)p.num_kv_heads * p.num_seqs * q.num_tiles;
+  if (nwg == 0) return hipSuccess;
+  if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), dim3((uint32_t)nwg), dim3(kMqWaves * 64), 0, st,
+                     q);
+  return hipGetLastError();
+}
+
+template <class DT, int D>
+hipError_t launch_pf_g(const PrefillParams& p, int group, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_pf<DT, D, 1>(p, st);
+    case 2: return launch_pf<DT, D, 2>(p, st);
+    case 4: return launch_pf<DT, D, 4>(p, st);
+    case 8: return launch_pf<DT, D, 8>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class DT>
+hipError_t launch_pf_d(const PrefillParams& p, int head_size, int group, hipStream_t st) {
+  switch (head_size) {
+    case 64: return launch_pf_g<DT, 64>(p, group, st);
+    case 128: return launch_pf_g<DT, 128>(p, group, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group,
+                          hipStream_t stream) {
+  return dtype == 0 ? launch_pf_d<Fp16>(p, head_size, group, stream)
+                    : launch_pf_d<Bf16>(p, head_size, group, stream);
+}
+
+hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream) {
+  if (p.num_seqs == 0 || p.max_query_len == 0) return hipSuccess;
+  const dim3 grid((p.max_query_len + kSlotThreads - 1) / kSlotThreads, p.num_seqs);
+  hipLaunchKernelGGL(prefill_slot_kernel, grid, dim3(kSlotThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

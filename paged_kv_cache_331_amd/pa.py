@@ -42,6 +42,10 @@ SIGNATURES = {
     "pa_decode_cascade": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
                                          _i32, _i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                          _vp]),
+    "pa_prefill_slot_mapping": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                               _i32, _vp, _vp]),
+    "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz,
                                      _vp]),
@@ -252,4 +256,42 @@ def decode_cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.
                                   int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
                                   _stream(stream))
     _check("pa_decode_cascade", st)
+    return out
+
+
+def prefill_slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         query_start: torch.Tensor, num_tokens: int, max_query_len: int,
+                         block_size: int, max_context_len: int,
+                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Slot of every new token of a prefill batch (int32 [num_tokens])."""
+    B, MB = block_tables.shape
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=block_tables.device)
+    st = load().pa_prefill_slot_mapping(_dev(block_tables, "block_tables"), MB,
+                                        _dev(context_lens, "context_lens"),
+                                        _dev(query_start, "query_start"), B, int(num_tokens),
+                                        int(max_query_len), int(block_size),
+                                        int(max_context_len), _dev(out, "slot_mapping"),
+                                        _stream(stream))
+    _check("pa_prefill_slot_mapping", st)
+    return out
+
+
+def prefill(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+            scale: float, max_query_len: int, max_context_len: int,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal paged attention of the new tokens (q, out: [num_tokens, Hq, D])."""
+    T, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    B, MB = block_tables.shape
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().pa_prefill(_dev(q, "q"), _dev(key_cache, "key_cache"),
+                           _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+                           _dev(context_lens, "context_lens"), _dev(query_start, "query_start"),
+                           float(scale), _dev(out, "out"), B, T, int(max_query_len), Hq, Hkv, D,
+                           bs, NB, MB, int(max_context_len), dtype_code(q.dtype),
+                           _stream(stream))
+    _check("pa_prefill", st)
     return out

@@ -30,7 +30,8 @@ def test_header_declares_expected_api():
                                   "pa_cache_write", "pa_decode_workspace_size",
                                   "pa_decode_partition_size", "pa_decode", "pa_cache_write_fp8",
                                   "pa_decode_fp8", "pa_decode_cascade",
-                                  "pa_decode_cascade_workspace_size"])
+                                  "pa_decode_cascade_workspace_size", "pa_prefill",
+                                  "pa_prefill_slot_mapping"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -246,3 +247,30 @@ def test_cascade_validation(lib, kw, code):
                                      a["MB"], a["maxlen"], a["pfx"], a["P"], a["dtype"], a["ws"],
                                      a["wss"], a["stream"])
     assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3),
+    (dict(T=-1), -2),
+    (dict(maxlen=65), -2),
+    (dict(D=96), -4),
+    (dict(Hq=12, Hkv=4), -4),
+    (dict(qs=None), -1),
+    (dict(out=8), -4),
+])
+def test_prefill_validation(lib, kw, code):
+    a = dict(q=16, kc=16, vc=16, bt=16, lens=16, qs=16, scale=0.125, out=16, B=2, T=10, mq=8,
+             Hq=4, Hkv=4, D=128, bs=16, NB=10, MB=4, maxlen=64, dtype=F, stream=None)
+    a.update(kw)
+    st = pa.load().pa_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["qs"], a["scale"],
+                              a["out"], a["B"], a["T"], a["mq"], a["Hq"], a["Hkv"], a["D"],
+                              a["bs"], a["NB"], a["MB"], a["maxlen"], a["dtype"], a["stream"])
+    assert st == code
+
+
+def test_prefill_zero_work_is_ok(lib):
+    assert pa.load().pa_prefill(None, None, None, None, None, None, 0.1, None, 0, 0, 0, 4, 4, 128,
+                                16, 10, 4, 64, F, None) == 0
+    assert pa.load().pa_prefill_slot_mapping(None, 4, None, None, 0, 0, 0, 16, 64, None,
+                                             None) == 0
+    assert pa.load().pa_prefill_slot_mapping(16, 4, 16, 16, 2, 10, 8, 16, 65, 16, None) == -2

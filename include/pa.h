@@ -57,7 +57,9 @@ enum pa_status {
   PA_ERR_UNSUPPORTED = -4, /* valid, but no kernel built for this head size,
                               block size, group size or partition size            */
   PA_ERR_WORKSPACE = -5,   /* split-K workspace missing or too small              */
-  PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed          */
+  PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed          */
+  PA_ERR_NO_BLOCKS = -7,   /* block pool: fewer free blocks than requested         */
+  PA_ERR_STATE = -8        /* block pool: block not allocated / freed too often    */
 };
 
 /* Supported shapes: head_size in {64, 128}; block_size in {16, 32};
@@ -353,6 +355,61 @@ PA_API int pa_prefill(const void* q, const void* key_cache, const void* value_ca
                       int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                       int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t dtype, void* stream);
+
+/*
+ * Host block pool -- the bookkeeping that produces the tables (host memory
+ * only; no device work). A block's reference count says how many tables
+ * point at it ("PagedAttention 机制" §5.3.4 BlockAllocator). The free list is
+ * a queue: allocation takes blocks from its head, and a block whose count
+ * drops to 0 joins its tail, so the least recently freed block is reused
+ * first ("01. PagedAttention 详解" 自检 Q3). A new pool has every block free,
+ * in id order. A pool is not thread-safe: one caller at a time.
+ */
+typedef struct pa_pool pa_pool;
+
+/* A pool of num_blocks blocks, all free; NULL if num_blocks < 1 or out of
+   host memory. */
+PA_API pa_pool* pa_pool_create(int32_t num_blocks);
+PA_API void pa_pool_destroy(pa_pool* pool);
+/* Free blocks (-1 for a NULL pool). */
+PA_API int32_t pa_pool_num_free(const pa_pool* pool);
+/* Reference count of a block (0 = free; -1 for a NULL pool or id out of range). */
+PA_API int32_t pa_pool_ref_count(const pa_pool* pool, int32_t block);
+/* n blocks from the head of the free queue, count 1 each, into blocks[0..n).
+   PA_ERR_NO_BLOCKS (nothing taken) when fewer than n are free. */
+PA_API int pa_pool_allocate(pa_pool* pool, int32_t n, int32_t* blocks);
+/* One reference fewer for each listed block (a block may be listed as often
+   as it is referenced); a block reaching 0 joins the queue's tail.
+   PA_ERR_STATE (nothing changed) for a free block or an id out of range. */
+PA_API int pa_pool_free(pa_pool* pool, const int32_t* blocks, int32_t n);
+/* One reference more for each listed block (another table points at it).
+   PA_ERR_STATE (nothing changed) for a free block or an id out of range. */
+PA_API int pa_pool_share(pa_pool* pool, const int32_t* blocks, int32_t n);
+/* Copy-on-write before a write into *block ("01. PagedAttention 详解" §6):
+   returns 0 if *block has one reference (write in place); returns 1 after
+   taking a fresh block from the queue's head, dropping one reference of the
+   shared block, setting *src = old block, *dst = fresh block and
+   *block = fresh block -- the caller then copies src to dst (pa_copy_blocks)
+   and stores *block in its table. PA_ERR_STATE for a free block,
+   PA_ERR_NO_BLOCKS when a copy is needed and no block is free. */
+PA_API int pa_pool_copy_on_write(pa_pool* pool, int32_t* block, int32_t* src, int32_t* dst);
+
+/*
+ * pa_copy_blocks -- whole-block copies in both caches (device work).
+ * For each i < num_pairs: block block_pairs[2i+1] := block block_pairs[2i]
+ * of key_cache and of value_cache, every position and head (the copy of
+ * pa_pool_copy_on_write). block_pairs: int32 [num_pairs, 2] (device).
+ * elem_bytes: 2 for fp16 / bf16 caches, 1 for FP8 caches. Destinations must
+ * be distinct and no destination may be a source of the same call. Pairs
+ * with an id outside [0, num_blocks) are skipped. Bit-exact copy.
+ * Errors: PA_ERR_SHAPE, PA_ERR_DTYPE (elem_bytes), PA_ERR_UNSUPPORTED (block
+ * bytes not a multiple of 16, caches not 16-byte aligned), PA_ERR_NULL,
+ * PA_ERR_HIP. num_pairs == 0 returns PA_OK.
+ */
+PA_API int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                          int32_t num_pairs, int64_t num_blocks, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_size, int32_t elem_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -226,6 +226,9 @@ const char* pa_status_string(int status) {
                                     "partition size or pointer alignment";
     case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
     case PA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
+    case PA_ERR_STATE: return "the block is not allocated in the pool (or freed more often than "
+                              "it is referenced)";
     default: return "unknown status";
   }
 }
@@ -486,6 +489,23 @@ int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
   p.len_cap = max_context_len;
   p.num_blocks = num_blocks;
   const hipError_t e = pa::launch_prefill(p, dtype, head_size, group, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+
+int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                   int32_t num_pairs, int64_t num_blocks, int32_t block_size,
+                   int32_t num_kv_heads, int32_t head_size, int32_t elem_bytes, void* stream) {
+  if (num_pairs < 0 || num_blocks < 0 || block_size < 1 || num_kv_heads < 1 || head_size < 1)
+    return PA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_DTYPE;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_size * elem_bytes;
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_pairs) return PA_ERR_NULL;
+  if (!aligned16(key_cache) || !aligned16(value_cache)) return PA_ERR_UNSUPPORTED;
+  const hipError_t e = pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs,
+                                              num_blocks, block_bytes, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

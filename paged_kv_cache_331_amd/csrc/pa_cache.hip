@@ -98,7 +98,45 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_fp8_kernel(
       encode_fp8x8<ST>(*reinterpret_cast<const uint4*>(v + src), v_scale);
 }
 
+// Whole-block copies for copy-on-write: block dst := block src of both
+// caches (every position and head). Work-group (pair, 16 KB slab); threads
+// copy 16 bytes each, coalesced; pairs with an out-of-range id are skipped.
+constexpr int kCopyThreads = 256;
+constexpr int64_t kCopySlab = kCopyThreads * 16 * 4;   // bytes per work-group and cache
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ pairs,
+    int64_t num_blocks, int64_t block_bytes, int32_t slabs) {
+  const int pair = blockIdx.x / slabs;
+  const int slab = blockIdx.x % slabs;
+  const int32_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if ((uint64_t)(uint32_t)src >= (uint64_t)num_blocks ||
+      (uint64_t)(uint32_t)dst >= (uint64_t)num_blocks)
+    return;
+  const int64_t off0 = (int64_t)slab * kCopySlab;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t off = off0 + ((int64_t)u * kCopyThreads + threadIdx.x) * 16;
+    if (off >= block_bytes) break;
+    *reinterpret_cast<uint4*>(kc + dst * block_bytes + off) =
+        *reinterpret_cast<const uint4*>(kc + src * block_bytes + off);
+    *reinterpret_cast<uint4*>(vc + dst * block_bytes + off) =
+        *reinterpret_cast<const uint4*>(vc + src * block_bytes + off);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int32_t num_pairs,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t slabs = (block_bytes + kCopySlab - 1) / kCopySlab;
+  const int64_t grid = (int64_t)num_pairs * slabs;
+  if (grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)grid), dim3(kCopyThreads), 0, stream,
+                     (uint8_t*)kc, (uint8_t*)vc, pairs, num_blocks, block_bytes, (int32_t)slabs);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const int32_t* bt, int32_t max_blocks_per_seq, const int32_t* lens,
                                int32_t num_seqs, int32_t block_size, int32_t* slots,

@@ -91,6 +91,11 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, uint16_t* kc
                               const int32_t* slots, int32_t num_tokens, int64_t num_slots,
                               int32_t row_elems, hipStream_t stream);
 
+// Block copies for copy-on-write: for each pair, block pairs[2i+1] := block
+// pairs[2i] of both caches; block_bytes = block_size * Hkv * D * element bytes.
+hipError_t launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int32_t num_pairs,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
 // Quantizing write into an FP8 E4M3 cache: code = e4m3(fp32(x) / scale).
 hipError_t launch_cache_write_fp8(const uint16_t* k, const uint16_t* v, uint8_t* kc, uint8_t* vc,
                                   const int32_t* slots, int32_t num_tokens, int64_t num_slots,

@@ -20,7 +20,8 @@ PA_DTYPE_FP16 = 0
 PA_DTYPE_BF16 = 1
 PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
-          -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP"}
+          -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP",
+          -7: "PA_ERR_NO_BLOCKS", -8: "PA_ERR_STATE"}
 
 _i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_void_p, ctypes.c_size_t)
@@ -46,6 +47,15 @@ SIGNATURES = {
                                                _i32, _vp, _vp]),
     "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp]),
+    "pa_pool_create": (_vp, [_i32]),
+    "pa_pool_destroy": (None, [_vp]),
+    "pa_pool_num_free": (_i32, [_vp]),
+    "pa_pool_ref_count": (_i32, [_vp, _i32]),
+    "pa_pool_allocate": (ctypes.c_int, [_vp, _i32, _vp]),
+    "pa_pool_free": (ctypes.c_int, [_vp, _vp, _i32]),
+    "pa_pool_share": (ctypes.c_int, [_vp, _vp, _i32]),
+    "pa_pool_copy_on_write": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz,
                                      _vp]),
@@ -295,3 +305,64 @@ def prefill(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                            _stream(stream))
     _check("pa_prefill", st)
     return out
+
+
+class BlockPool:
+    """The library's host block pool (reference counts, free queue, copy-on-write)."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = load()
+        self._h = self._lib.pa_pool_create(int(num_blocks))
+        if not self._h:
+            raise ValueError("pa_pool_create failed")
+        self.num_blocks = int(num_blocks)
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_pool_num_free(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(self._lib.pa_pool_ref_count(self._h, int(block)))
+
+    def allocate(self, n: int):
+        buf = (ctypes.c_int32 * max(n, 1))()
+        _check("pa_pool_allocate", self._lib.pa_pool_allocate(self._h, int(n), buf))
+        return list(buf[:n])
+
+    def free(self, blocks) -> None:
+        arr = (ctypes.c_int32 * max(len(blocks), 1))(*blocks)
+        _check("pa_pool_free", self._lib.pa_pool_free(self._h, arr, len(blocks)))
+
+    def share(self, blocks) -> None:
+        arr = (ctypes.c_int32 * max(len(blocks), 1))(*blocks)
+        _check("pa_pool_share", self._lib.pa_pool_share(self._h, arr, len(blocks)))
+
+    def copy_on_write(self, block: int):
+        """(block to write into, (src, dst) copy or None)."""
+        b, s, d = ctypes.c_int32(int(block)), ctypes.c_int32(-1), ctypes.c_int32(-1)
+        st = self._lib.pa_pool_copy_on_write(self._h, ctypes.byref(b), ctypes.byref(s),
+                                             ctypes.byref(d))
+        if st < 0:
+            raise PagedAttentionError("pa_pool_copy_on_write", st)
+        return b.value, ((s.value, d.value) if st == 1 else None)
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,
+                stream=None) -> None:
+    """block dst := block src of both caches for every row (src, dst) of block_pairs."""
+    NB, bs, Hkv, D = key_cache.shape
+    n = block_pairs.shape[0] if block_pairs.numel() else 0
+    st = load().pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                               _dev(block_pairs, "block_pairs") if n else None, n, NB, bs, Hkv,
+                               D, key_cache.element_size(), _stream(stream))
+    _check("pa_copy_blocks", st)

@@ -31,7 +31,10 @@ def test_header_declares_expected_api():
                                   "pa_decode_partition_size", "pa_decode", "pa_cache_write_fp8",
                                   "pa_decode_fp8", "pa_decode_cascade",
                                   "pa_decode_cascade_workspace_size", "pa_prefill",
-                                  "pa_prefill_slot_mapping"])
+                                  "pa_prefill_slot_mapping", "pa_pool_create",
+                                  "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count",
+                                  "pa_pool_allocate", "pa_pool_free", "pa_pool_share",
+                                  "pa_pool_copy_on_write", "pa_copy_blocks"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -274,3 +277,18 @@ def test_prefill_zero_work_is_ok(lib):
     assert pa.load().pa_prefill_slot_mapping(None, 4, None, None, 0, 0, 0, 16, 64, None,
                                              None) == 0
     assert pa.load().pa_prefill_slot_mapping(16, 4, 16, 16, 2, 10, 8, 16, 65, 16, None) == -2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), -2),
+    (dict(eb=4), -3),
+    (dict(D=4, bs=1, Hkv=1), -4),        # 8-byte blocks
+    (dict(kc=None), -1),
+    (dict(vc=8), -4),
+])
+def test_copy_blocks_validation(lib, kw, code):
+    a = dict(kc=16, vc=16, pairs=16, n=2, NB=8, bs=16, Hkv=2, D=64, eb=2, stream=None)
+    a.update(kw)
+    st = pa.load().pa_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["NB"], a["bs"],
+                                  a["Hkv"], a["D"], a["eb"], a["stream"])
+    assert st == code

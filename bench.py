@@ -443,7 +443,8 @@ def main(argv=None) -> int:
     dec_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_per_step = wall * 1e3 / args.steps
     decode_ms = float(np.mean(dec_ms))
-    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode {decode_ms:.4f} ms",
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode mean {decode_ms:.4f} ms"
+          f" (median {np.median(dec_ms):.4f}, min {np.min(dec_ms):.4f}, max {np.max(dec_ms):.4f})",
           file=sys.stderr, flush=True)
 
     copy = copy_bandwidth()

@@ -150,8 +150,9 @@ PA_API int pa_cache_write_fp8(const void* k, const void* v, void* key_cache, voi
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs.
  *
  * partition_size < 0 (single pass) needs none (returns 0). partition_size > 0
- * needs room for the fp32 partials of ceil(max_context_len / partition_size)
- * partitions per (sequence, query head). partition_size == 0 (automatic)
+ * needs 256 bytes of scheduler state and room for the fp32 partials of
+ * ceil(max_context_len / partition_size) partitions per (sequence, query
+ * head). partition_size == 0 (automatic)
  * returns the most any automatic choice can use. Pure host arithmetic.
  * Returns 0 for invalid (negative) sizes.
  */
@@ -212,7 +213,14 @@ PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
  * workspace : device buffer, 256-byte aligned, of at least
  *             pa_decode_workspace_size(...) bytes for the same sizes and
  *             partition_size (may be NULL when that size is 0). Its contents
- *             need no initialisation; it is scratch for this call only.
+ *             need no initialisation. Its first 256 bytes carry
+ *             scheduler state from one split call to the next on the same
+ *             buffer (a 64-bit word: a tag in bytes 0-3, a work counter that
+ *             every call returns to zero in bytes 4-7); a call that finds no
+ *             such state (a fresh buffer, or one overwritten since) gives
+ *             the same result with a fixed schedule. The rest is scratch
+ *             for this call only. Calls that
+ *             run at the same time need distinct workspaces.
  * Errors: PA_ERR_DTYPE; PA_ERR_SHAPE (non-positive head counts or sizes,
  * num_q_heads not a multiple of num_kv_heads, max_context_len above
  * max_blocks_per_seq * block_size, non-finite scale); PA_ERR_UNSUPPORTED
@@ -251,10 +259,11 @@ PA_API int pa_decode_fp8(const void* q, const void* key_cache, const void* value
 /*
  * pa_decode_cascade_workspace_size -- workspace bytes of pa_decode_cascade.
  *
- * Room for the fp32 partials of ceil(prefix_len / 256) prefix chunks plus the
- * partitions of the positions past the prefix (as pa_decode_workspace_size
- * counts them for max_context_len - prefix_len tokens), per (sequence, query
- * head), with prefix_len = shared_prefix_blocks * block_size. With
+ * 256 bytes of scheduler state, and room for the fp32 partials of
+ * ceil(prefix_len / 128) prefix chunks plus the partitions of the positions
+ * past the prefix (as pa_decode_workspace_size counts them for
+ * max_context_len - prefix_len tokens), per (sequence, query head), with
+ * prefix_len = shared_prefix_blocks * block_size. With
  * shared_prefix_blocks == 0 it equals pa_decode_workspace_size. Pure host
  * arithmetic; 0 for invalid sizes.
  */
@@ -287,7 +296,7 @@ PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_h
  * is range-checked).
  * shared_prefix_blocks : 0 .. max_blocks_per_seq (0 = a plain pa_decode call)
  * workspace            : at least pa_decode_cascade_workspace_size(...) bytes,
- *                        256-byte aligned; scratch for this call only
+ *                        256-byte aligned; used as pa_decode uses its workspace
  * Errors: those of pa_decode, and PA_ERR_SHAPE for shared_prefix_blocks out
  * of range. Caches of the query's 2-byte type only.
  */

@@ -65,8 +65,17 @@ union Vec16 {
   uint32_t w[4];
 };
 
+template <int D, int G>
+struct DecodeLds {
+  int32_t tbl[kTableChunk];
+  float part[kDecodeWaves][G][D + 2];
+};
+
+// One work item: kv head g, sequence s, partition p. Uniform over the
+// work-group (every thread takes the same path and the same barriers).
 template <class DT, class KT, int D, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
+__device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
+                                            DecodeLds<D, G>& sm) {
   using S = Storage<DT>;
   using KV = Kv<DT, KT>;
   using elem = typename KV::elem;
@@ -79,21 +88,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   constexpr int NT = NW * 64;
   static_assert(D == 64 || D == 128, "head size");
 
-  __shared__ int32_t s_tbl[kTableChunk];
-  __shared__ float s_part[NW][G][D + 2];
-
-  // Work-groups are numbered kv head fastest. With many (sequence, kv head)
-  // pairs the partition index comes last: every sequence's first partition
-  // is dispatched before any second one, and partitions past a sequence's
-  // end (which exit at once) gather at the end of the grid. With few pairs
-  // (long contexts) the sequence index comes last, so one sequence's
-  // partitions run together; each order measured faster in its regime.
+  int32_t* s_tbl = sm.tbl;
+  auto& s_part = sm.part;
   const int Hkv = a.num_kv_heads;
-  int wg = blockIdx.x;
-  const int g = wg % Hkv;
-  wg /= Hkv;
-  const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
-  const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
 
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
@@ -289,6 +286,68 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   }
 }
 
+// One work-group per item. Work-groups are numbered kv head fastest. With
+// many (sequence, kv head) pairs the partition index comes last: every
+// sequence's first partition is dispatched before any second one, and
+// partitions past a sequence's end (which exit at once) gather at the end of
+// the grid. With few pairs (long contexts) the sequence index comes last, so
+// one sequence's partitions run together; each order measured faster in its
+// regime.
+template <class DT, class KT, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
+  __shared__ DecodeLds<D, G> sm;
+  int wg = blockIdx.x;
+  const int g = wg % a.num_kv_heads;
+  wg /= a.num_kv_heads;
+  const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
+  const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
+  decode_item<DT, KT, D, G>(a, g, s, p, sm);
+}
+
+// Persistent grid: gridDim.x (at most the item count) work-groups walk the
+// items in partition-major order (kv head fastest, then sequence). Each
+// starts with item blockIdx.x; later items come from the counter half of the
+// scheduler word as grid + ticket, so a work-group that drew short items
+// takes more of them and none waits on a hardware dispatch slot. The counter
+// is trusted only when the word's tag half holds sched_tag, which the combine
+// kernel writes together with counter = 0 after every call; otherwise (the
+// first call on a workspace) the items are walked with the fixed stride
+// gridDim.x. Every item is taken by exactly one work-group under either
+// schedule. One counter serves the whole chip: splitting it per XCD (each
+// XCD's work-groups on their own share of the items, with or without
+// stealing at the end) measured 3-9% slower.
+template <class DT, class KT, int D, int G>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
+  __shared__ DecodeLds<D, G> sm;
+  __shared__ int s_item[2];
+  const int Hkv = a.num_kv_heads;
+  const int total = Hkv * a.num_seqs * a.num_parts;
+  const uint32_t grid = gridDim.x;                 // <= total (host)
+  const bool counted = (uint32_t)*a.sched == a.sched_tag;
+  int64_t item = blockIdx.x;
+  for (int k = 0; item < total; k ^= 1) {
+    const int it = (int)item;
+    const int g = it % Hkv;
+    const int s = (it / Hkv) % a.num_seqs;
+    const int p = it / (Hkv * a.num_seqs);
+    decode_item<DT, KT, D, G>(a, g, s, p, sm);
+    if (!counted) {
+      item += grid;
+      continue;
+    }
+    // Double-buffered slot: a thread still reading s_item[k] from the previous
+    // round cannot be overtaken, since thread 0 writes s_item[k] again only
+    // after the barrier below has been passed by every thread. A ticket past
+    // the last item (whatever the counter held) ends the walk.
+    if (threadIdx.x == 0) {
+      const uint32_t t = (uint32_t)(atomicAdd(a.sched, 1ull << 32) >> 32);
+      s_item[k] = t < (uint32_t)total - grid ? (int)(grid + t) : total;
+    }
+    __syncthreads();
+    item = s_item[k];
+  }
+}
+
 // Split-K combine for the sequences with two or more partitions:
 //   out = sum_q 2^(m_q - M) o_q / sum_q 2^(m_q - M) l_q,   M = max_q m_q,
 // over the partitions q that hold tokens. One work-group per (sequence,
@@ -309,6 +368,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int h = blockIdx.x % a.num_q_heads;
   const int s = blockIdx.x / a.num_q_heads;
   const int tid = threadIdx.x;
+  // The partition kernel has finished (stream order): leave the scheduler
+  // state the next persistent launch on this workspace expects.
+  if (a.sched != nullptr && blockIdx.x == 0 && tid == 0) *a.sched = a.sched_tag;
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int64_t oh = (int64_t)s * a.num_q_heads + h;
@@ -376,9 +438,24 @@ hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   const uint64_t nwg = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G>), dim3((uint32_t)nwg),
-                     dim3(kDecodeWaves * 64), 0, st, a);
-  if (a.num_parts == 1 && !a.always_combine) return hipGetLastError();
+  const bool combine = a.num_parts > 1 || a.always_combine;
+  if (a.sched != nullptr && combine && a.persist_grid > 0) {
+    const uint32_t grid = (uint32_t)(nwg < (uint64_t)a.persist_grid ? nwg : a.persist_grid);
+    hipLaunchKernelGGL((decode_persistent_kernel<DT, KT, D, G>), dim3(grid),
+                       dim3(kDecodeWaves * 64), 0, st, a);
+  } else {
+    DecodeParams b = a;
+    b.sched = nullptr;                   // the combine leaves the scheduler words alone
+    hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G>), dim3((uint32_t)nwg),
+                       dim3(kDecodeWaves * 64), 0, st, b);
+    if (!combine) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const uint64_t nr = (uint64_t)b.num_q_heads * b.num_seqs;
+    hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), dim3((uint32_t)nr), dim3(kReduceThreads), 0,
+                       st, b);
+    return hipGetLastError();
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t nr = (uint64_t)a.num_q_heads * a.num_seqs;

@@ -42,10 +42,27 @@ struct DecodeParams {
   int32_t prefix_chunks;    // prefix key chunks = partial slots 0 .. prefix_chunks-1
   int32_t prefix_row_tiles; // 64-row tiles of the num_seqs * group query rows
   int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
+  // Persistent scheduling (split calls whose combine kernel runs): the
+  // partition kernel is launched with persist_grid work-groups that take the
+  // (kv head, sequence, partition) items from the scheduler word *sched: low
+  // 32 bits a tag, high 32 bits a work counter. The combine kernel leaves it
+  // at (tag = sched_tag, counter = 0) for the next call; a partition kernel
+  // that finds another tag (a fresh or overwritten workspace) walks the items
+  // with a fixed stride instead. The tag sits at the lower address, so a
+  // write that reaches the counter from below clobbers the tag first.
+  unsigned long long* sched;  // nullptr: one work-group per item
+  uint32_t sched_tag;
+  int32_t persist_grid;       // 0: one work-group per item
 };
 
+// Bytes reserved for the scheduler word at the head of a split-K workspace,
+// before the partials.
+constexpr int kSchedBytes = 256;
+
 // Work-groups of the partition kernel per launch: one per
-// (kv head, partition, sequence). Launch shapes are fixed per instantiation.
+// (kv head, partition, sequence), or a persistent grid of a few per compute
+// unit that takes the items from a counter. Launch shapes are fixed per
+// instantiation.
 constexpr int kDecodeWaves = 4;
 constexpr int kReduceThreads = 256;
 

@@ -107,10 +107,11 @@ def test_decode_empty_batch_is_ok(lib):
 def test_workspace_size_arithmetic(lib):
     ws = pa.load().pa_decode_workspace_size
     assert ws(4, 32, 128, 100000, -1) == 0
-    # 4 * 32 * ceil(100000/512) = 25088 partials: m and l (fp32, 256-aligned) + o (fp32 x 128)
+    # 256 bytes for the scheduler word, then 4 * 32 * ceil(100000/512) = 25088 partials:
+    # m and l (fp32, 256-aligned) + o (fp32 x 128)
     n = 4 * 32 * 196
     al = lambda x: (x + 255) // 256 * 256
-    assert ws(4, 32, 128, 100000, 512) == 2 * al(4 * n) + al(4 * n * 128)
+    assert ws(4, 32, 128, 100000, 512) == 256 + 2 * al(4 * n) + al(4 * n * 128)
     assert ws(4, 32, 128, 100000, 0) == ws(4, 32, 128, 100000, 256)
     assert ws(-1, 32, 128, 10, 16) == 0
 
@@ -227,7 +228,7 @@ def test_cascade_workspace_arithmetic(lib):
     # 128 sequences x 32 heads; prefix 32 blocks of 32 = 1024 tokens -> 8 chunks of 128;
     # suffix up to 1536 - 1024 = 512 tokens in partitions of 256 -> 2; 10 slots
     n = 128 * 32 * 10
-    assert ws(128, 32, 128, 32, 1536, 32, 256) == 2 * al(4 * n) + al(4 * n * 128)
+    assert ws(128, 32, 128, 32, 1536, 32, 256) == 256 + 2 * al(4 * n) + al(4 * n * 128)
     assert ws(128, 32, 128, 32, 1536, 0, 256) == pa.load().pa_decode_workspace_size(
         128, 32, 128, 1536, 256)
     assert ws(-1, 32, 128, 32, 1536, 32, 256) == 0

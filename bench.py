@@ -35,7 +35,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
 METRIC = "decode attn tokens/s + effective KV HBM GB/s (% of MI355X peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ("paged_kv_cache_331_amd/csrc/pa_decode.hip",
-                  "paged_kv_cache_331_amd/csrc/pa_device.h")
+                  "paged_kv_cache_331_amd/csrc/pa_device.h",
+                  "paged_kv_cache_331_amd/csrc/pa_launch.h",
+                  "paged_kv_cache_331_amd/csrc/pa_cascade.hip",
+                  "paged_kv_cache_331_amd/csrc/pa_mq.h",
+                  "paged_kv_cache_331_amd/csrc/pa_api.hip")
 
 
 def algorithmic_bytes(spec, context_lens: np.ndarray) -> dict:
@@ -100,8 +104,9 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
     Each counter is scaled by what it reads for a device copy of
     ``copy_bytes`` (the calibration run, ``--copy-probe``): the copy fetches
     and writes exactly ``copy_bytes``. A decode call is the partition kernel
-    plus, when split, the reduce kernel; the median over dispatches of each
-    is summed. The record is keyed to the kernel sources' hash so that it
+    (one work-group per item, or the persistent grid) plus, when split, the
+    reduce kernel, and in a cascade the shared-prefix kernel before them; the
+    median over dispatches of each is summed. The record is keyed to the kernel sources' hash so that it
     stops being reported once the kernels change.
     """
     def median_kib(path, counter, match):
@@ -118,7 +123,8 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
     rec = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_fetch,
            "write_scale": f_write, "kernels": {}}
     total = 0.0
-    for tag in ("decode_partition_kernel", "decode_reduce_kernel"):
+    for tag in ("cascade_prefix_kernel", "decode_partition_kernel", "decode_persistent_kernel",
+                "decode_reduce_kernel"):
         m = lambda k, tag=tag: tag in k
         try:
             fk, n = median_kib(fetch_csv, "FETCH_SIZE", m)

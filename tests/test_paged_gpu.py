@@ -103,16 +103,21 @@ def test_decode_small_all_outputs(name, P):
 SAMPLES = 6
 
 
-@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
-def test_decode_full_size_sampled(name):
+FULL_CASES = [(n, 0) for n in wl.CONFIG_ORDER] + [
+    (n, wl.CONFIGS[n].partition_size) for n in wl.CONFIG_ORDER if wl.CONFIGS[n].partition_size]
+
+
+@pytest.mark.parametrize("name,P", FULL_CASES)
+def test_decode_full_size_sampled(name, P):
     """Full-size workload in the benchmark's launch configuration (automatic
-    variant choice, cache write first); sampled (sequence, head) outputs are
-    recomputed by the oracle one by one."""
+    variant choice, cache write first), and in the partition size the
+    workload is quoted with where it names one; sampled (sequence, head)
+    outputs are recomputed by the oracle one by one."""
     spec = wl.CONFIGS[name]
     b = wl.make_batch(spec)
-    say(f"decode full {name} B={b.num_seqs} NB={b.num_blocks} maxlen={b.max_context_len}")
+    say(f"decode full {name} B={b.num_seqs} NB={b.num_blocks} maxlen={b.max_context_len} P={P}")
     d = Device(b)
-    _, out = gpu_step(b, d, write=spec.cache_write, partition_size=0)
+    _, out = gpu_step(b, d, write=spec.cache_write, partition_size=P)
     kc, vc, _ = oracle_caches(b, spec.cache_write)
     outf = out.float().cpu().numpy()
     assert np.all(np.isfinite(outf))

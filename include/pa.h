@@ -298,7 +298,8 @@ PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_h
  * workspace            : at least pa_decode_cascade_workspace_size(...) bytes,
  *                        256-byte aligned; used as pa_decode uses its workspace
  * Errors: those of pa_decode, and PA_ERR_SHAPE for shared_prefix_blocks out
- * of range. Caches of the query's 2-byte type only.
+ * of range or (with shared_prefix_blocks > 0 and num_seqs > 0) num_blocks
+ * == 0. Caches of the query's 2-byte type only.
  */
 PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* value_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
@@ -354,8 +355,9 @@ PA_API int pa_prefill_slot_mapping(const int32_t* block_tables, int32_t max_bloc
  * Only table entries of positions < L are read; block ids outside
  * [0, num_blocks) read as zeros. No workspace is needed.
  * Errors: as pa_decode (dtype, shapes, head size 64 / 128, block size
- * 16 / 32, group 1 / 2 / 4 / 8, alignment, NULL, HIP). num_seqs, num_tokens
- * or max_query_len == 0 returns PA_OK.
+ * 16 / 32, group 1 / 2 / 4 / 8, alignment, NULL, HIP), and PA_ERR_SHAPE for
+ * num_blocks == 0 when there are new tokens (they live in the pool).
+ * num_seqs, num_tokens or max_query_len == 0 returns PA_OK.
  */
 PA_API int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, const int32_t* context_lens,

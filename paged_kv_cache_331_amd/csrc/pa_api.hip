@@ -405,6 +405,9 @@ int pa_decode_cascade(const void* q, const void* key_cache, const void* value_ca
   if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
+  // A shared prefix lives in the pool; the matrix-core kernel also relies on
+  // slot 0 existing (a masked position reads it).
+  if (num_blocks < 1) return PA_ERR_SHAPE;
   if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
@@ -503,6 +506,9 @@ int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
   if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
   if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  // New tokens were written into the pool, so it has blocks; the matrix-core
+  // kernel also relies on slot 0 existing (a masked position reads it).
+  if (num_blocks < 1) return PA_ERR_SHAPE;
   if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start ||
       !out)
     return PA_ERR_NULL;

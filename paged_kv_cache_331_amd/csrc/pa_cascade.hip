@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const Dec
   const int grp = lane >> 4;
 
   const int R = a.num_seqs * G;          // query rows of kv head g
-  const int r = rt * kMqRowsPerWg + wave * kMqRowsPerWave + j;
+  const int r = rt * kMqWaves * kMqRowsPerBlock + wave * kMqRowsPerBlock + j;
   const bool row_ok = r < R;
   const int s = row_ok ? r / G : 0;
   const int h = g * G + (row_ok ? r % G : 0);
@@ -84,31 +84,34 @@ __global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const Dec
   for (int w = 1; w < kMqWaves; ++w) wg_limit = max(wg_limit, s_limit[w]);
   const int kend = min(c1, wg_limit);
 
-  u32x4_t qb[D / 32];
-  mq_load_q<D>(qb, a.q + ((int64_t)s * a.num_q_heads + h) * D, row_ok);
-  MqState<D> st;
+  u32x4_t qb[1][D / 32];
+  mq_load_q<D>(qb[0], a.q + ((int64_t)s * a.num_q_heads + h) * D, row_ok);
+  MqState<D, 1> st;
   st.init();
   auto slot_of = [&](int t) -> int64_t {
     const int blk = s_tbl[(t >> lbs) - b0];
     return blk < 0 ? -1 : (int64_t)blk * bs + (t & (bs - 1));
   };
-  mq_attend<DT, D>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
-                   static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend,
-                   min(limit, c1), a.scale_log2, slot_of);
+  // Rows past the batch attend unmasked with q = 0 and are not written.
+  const int row_end[1] = {row_ok ? min(limit, c1) : kend};
+  mq_attend<DT, D, 1>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
+                      static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend, row_end,
+                      a.scale_log2, slot_of);
 
-  // Partial of this chunk for the row: (m, sum of weights, unnormalised O).
-  const float lsum = mq_sum_over_groups(st.lsum);
+  // Partial of this chunk for the row: (reference max, sum of weights,
+  // unnormalised O), consistent with one another whatever the reference.
+  const float lsum = mq_sum_over_groups(st.lsum[0]);
   if (!row_ok) return;
   const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.part_stride + chunk;
   if (grp == 0) {
-    a.ws_m[pi] = st.m;
+    a.ws_m[pi] = st.m[0];
     a.ws_l[pi] = lsum;
   }
   float* po = a.ws_o + pi * D + 4 * grp;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
     *reinterpret_cast<float4*>(po + 16 * dt) =
-        make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+        make_float4(st.acc[0][dt][0], st.acc[0][dt][1], st.acc[0][dt][2], st.acc[0][dt][3]);
 }
 
 template <class DT, int D, int G>

@@ -2,23 +2,34 @@
 // that share a kv head, attended to a range of positions reached through a
 // block table. Used by the cascade's shared-prefix kernel and by prefill.
 //
-// A work-group is 4 wave64s; each wave owns 16 query rows. With
+// A work-group is 4 wave64s; each wave owns RB blocks of 16 query rows. With
 // v_mfma_f32_16x16x32 (lane l: A row l%16, B column l%16, k = 8*(l/16)..+7;
-// C column l%16, rows 4*(l/16)..+3) one 32-key step computes
+// C column l%16, rows 4*(l/16)..+3) one 32-key step computes, per row block,
 //   S^T(16 keys x 16 queries)   = K(16 keys x D) . Q^T(D x 16 queries)   (two key tiles)
 //   O^T(16 dims x 16 queries)  += V^T(16 dims x 32 keys) . P^T(32 keys x 16 queries)
-// Each lane ends S^T holding the logits of ONE query (its column) for 4 keys
-// of each tile. Taking the k index of the step as keys {4g..4g+3} of the first
-// tile followed by {4g..4g+3} of the second (g = l/16) -- the sum over keys
-// does not care about their order -- those logits' softmax weights are
-// exactly the lane's own B operand for the V product, so no weight crosses
-// lanes. V^T is read from LDS in that key order.
+// Every K or V fragment read from LDS feeds all RB row blocks. Each lane ends
+// S^T holding the logits of ONE query (its column) for 4 keys of each tile.
+// Taking the k index of the step as keys {4g..4g+3} of the first tile
+// followed by {4g..4g+3} of the second (g = l/16) -- the sum over keys does
+// not care about their order -- those logits' softmax weights are exactly
+// the lane's own B operand for the V product, so no weight crosses lanes.
+// V^T is read from LDS in that key order.
+//
+// Softmax: online, in base 2, with a lazily moved reference. A row's
+// reference max m only moves when a step's max exceeds it by more than
+// kMqSlack (log2 units), so the weights 2^(s - m) stay below 2^kMqSlack and
+// the accumulators are rescaled only on such steps (and skipped by the whole
+// wave when none of its rows moved). The result sum 2^(s-m) v / sum 2^(s-m)
+// does not depend on m, so this is exact up to rounding. Steps whose keys lie
+// below every row's limit in the wave skip the masking.
 //
 // Memory: each step's K and V rows are read once per work-group with
 // coalesced 16-byte loads, two steps ahead of their use, into a
 // double-buffered LDS area: K row-major with the 16-byte chunk c of key row r
 // at chunk c ^ (r % 16) (the A-operand reads then spread over all banks), V
 // transposed as one 32-bit word per (dimension, key pair) in padded rows.
+// Loads never branch: a position with no slot reads slot 0, and zeros replace
+// it when it is staged.
 #pragma once
 
 #include "pa_device.h"
@@ -26,11 +37,15 @@
 namespace pa {
 
 constexpr int kMqWaves = 4;
-constexpr int kMqRowsPerWave = 16;
-constexpr int kMqRowsPerWg = kMqWaves * kMqRowsPerWave;
+constexpr int kMqRowsPerBlock = 16;           // query rows of one MFMA column block
 constexpr int kMqStep = 32;                   // keys per MFMA step
 constexpr int kMqVRow = kMqStep / 2 + 6;      // 32-bit key pairs per V^T row, padded
 constexpr float kMqEmptyMax = -1.0e30f;       // running max before any key (finite)
+constexpr float kMqSlack = 8.f;               // lazy reference: weights stay <= 2^8
+#ifndef PA_MQ_RING
+#define PA_MQ_RING 4
+#endif
+constexpr int kMqRing = PA_MQ_RING;           // steps of K/V loads in flight (registers)
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -42,11 +57,20 @@ template <> struct Mma<Fp16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
+  // Two weights in [0, 2^kMqSlack] rounded to nearest even, packed (lo, hi).
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
 };
 template <> struct Mma<Bf16> {
   static __device__ __forceinline__ f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
   }
 };
 
@@ -61,21 +85,24 @@ __device__ __forceinline__ float mq_sum_over_groups(float x) {
 }
 
 template <int D> struct MqLds {
-  uint16_t k[2][kMqStep][D];
-  uint32_t v[2][D][kMqVRow];
+  alignas(16) uint16_t k[2][kMqStep][D];
+  alignas(16) uint32_t v[2][D][kMqVRow];
 };
 
-// Running softmax state of one lane: its query column's max (identical in
-// the column's four lanes), this lane's share of the exp-sum, and its C
-// entries of O^T (dimensions 16*dt + 4*(lane/16) .. +3).
-template <int D> struct MqState {
-  f32x4_t acc[D / 16];
-  float m, lsum;
+// Running softmax state of one lane, per row block: its query column's
+// reference max (identical in the column's four lanes), this lane's share of
+// the exp-sum, and its C entries of O^T (dimensions 16*dt + 4*(lane/16) .. +3).
+template <int D, int RB> struct MqState {
+  f32x4_t acc[RB][D / 16];
+  float m[RB], lsum[RB];
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = kMqEmptyMax;
-    lsum = 0.f;
+    for (int b = 0; b < RB; ++b) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[b] = kMqEmptyMax;
+      lsum[b] = 0.f;
+    }
   }
 };
 
@@ -89,17 +116,17 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 }
 
 // Attend every row of the work-group to positions [c0, kend) of kv head g.
-// slot_of(t) gives position t's physical slot (or -1: a skipped block, read
-// as zeros). Keys >= row_end are masked for this lane's row; every position
-// below kend must hold finite data (a position some row of the work-group
-// may use). Must be reached by all threads of the work-group with the same
-// c0 / kend (it synchronises); LDS is free again when it returns.
-template <class DT, int D, class SlotOf>
-__device__ __forceinline__ void mq_attend(MqState<D>& st, const u32x4_t (&qb)[D / 32],
+// slot_of(t) gives position t's physical slot for c0 <= t < kend (or -1: a
+// skipped block, read as zeros). Keys >= row_end[b] are masked for this
+// lane's row of block b; every position below kend must hold finite data (a
+// position some row of the work-group may use). Must be reached by all
+// threads of the work-group with the same c0 / kend (it synchronises); LDS is
+// free again when it returns.
+template <class DT, int D, int RB, class SlotOf>
+__device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
                                           MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,
-                                          int64_t tok_stride, int g, int c0, int kend, int row_end,
-                                          float sl2, SlotOf slot_of) {
-  using S = Storage<DT>;
+                                          int64_t tok_stride, int g, int c0, int kend,
+                                          const int (&row_end)[RB], float sl2, SlotOf slot_of) {
   constexpr int NT = kMqWaves * 64;
   constexpr int KS = D / 32;
   constexpr int DTILES = D / 16;
@@ -113,110 +140,153 @@ __device__ __forceinline__ void mq_attend(MqState<D>& st, const u32x4_t (&qb)[D 
   const int grp = lane >> 4;
   const int kp = tid % 16;                     // V staging: key pair, 8 dimensions
   const int vd = (tid / 16) * 8;
-  const bool vthread = tid < 16 * CH;
-  struct Regs { u32x4_t k[KLOADS]; u32x4_t v[2]; };
-  Regs ring[2];
+  const bool vthread = tid < 16 * CH;          // uniform per wave
+  const uint16_t* kbase = kc + (int64_t)g * D;
+  const uint16_t* vbase = vc + (int64_t)g * D + vd;
+  // One ring slot: a step's loads in flight, and which of them hold a real
+  // slot (bit u: K chunk u, bit KLOADS + e: V row e). The zeros replace the
+  // others when the slot is staged, not at issue: using a load's result
+  // right away would make the wave wait for it there.
+  struct Regs { u32x4_t k[KLOADS]; u32x4_t v[2]; uint32_t ok; };
+  constexpr int RD = kMqRing;
+  static_assert(RD % 2 == 0, "ring depth");
+  Regs ring[RD];
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
 
+  // The wave's smallest row limit: a step entirely below it needs no mask.
+  int wmin = row_end[0];
+#pragma unroll
+  for (int b = 1; b < RB; ++b) wmin = min(wmin, row_end[b]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wmin = min(wmin, __shfl_xor(wmin, o));
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
+
+  auto slot = [&](int t) -> int64_t {
+    const int64_t sl = slot_of(t < kend ? t : kend - 1);
+    return t < kend ? sl : -1;
+  };
   auto issue = [&](int t0, Regs& rg) {
+    uint32_t ok = 0;
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int idx = tid + NT * u;
-      const int t = t0 + idx / CH;
-      const int64_t sl = t < kend ? slot_of(t) : -1;
-      rg.k[u] = sl >= 0 ? load_stream16(kc + sl * tok_stride + (int64_t)g * D + (idx % CH) * 8)
-                        : u32x4_t{0u, 0u, 0u, 0u};
+      const int64_t sl = slot(t0 + idx / CH);
+      rg.k[u] = load_stream16(kbase + (sl >= 0 ? sl : 0) * tok_stride + (idx % CH) * 8);
+      ok |= (sl >= 0 ? 1u : 0u) << u;
     }
+    if (vthread) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int t = t0 + 2 * kp + e;
-      const int64_t sl = (vthread && t < kend) ? slot_of(t) : -1;
-      rg.v[e] = sl >= 0 ? load_stream16(vc + sl * tok_stride + (int64_t)g * D + vd)
-                        : u32x4_t{0u, 0u, 0u, 0u};
+      for (int e = 0; e < 2; ++e) {
+        const int64_t sl = slot(t0 + 2 * kp + e);
+        rg.v[e] = load_stream16(vbase + (sl >= 0 ? sl : 0) * tok_stride);
+        ok |= (sl >= 0 ? 1u : 0u) << (KLOADS + e);
+      }
     }
+    rg.ok = ok;
   };
   auto stage = [&](const Regs& rg, int buf) {
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int idx = tid + NT * u;
       const int r = idx / CH, c = idx % CH;
-      *reinterpret_cast<u32x4_t*>(&lds.k[buf][r][(c ^ (r % CH16)) * 8]) = rg.k[u];
+      *reinterpret_cast<u32x4_t*>(&lds.k[buf][r][(c ^ (r % CH16)) * 8]) =
+          (rg.ok >> u) & 1u ? rg.k[u] : zero;
     }
     if (vthread) {
+      const u32x4_t v0 = (rg.ok >> KLOADS) & 1u ? rg.v[0] : zero;
+      const u32x4_t v1 = (rg.ok >> (KLOADS + 1)) & 1u ? rg.v[1] : zero;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lds.v[buf][vd + 2 * e][kp] = (rg.v[0][e] & 0xffffu) | (rg.v[1][e] << 16);
-        lds.v[buf][vd + 2 * e + 1][kp] = (rg.v[0][e] >> 16) | (rg.v[1][e] & 0xffff0000u);
+        lds.v[buf][vd + 2 * e][kp] = (v0[e] & 0xffffu) | (v1[e] << 16);
+        lds.v[buf][vd + 2 * e + 1][kp] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
       }
     }
   };
   auto compute = [&](int t0, int buf) {
-    float lg[2][4];
+    f32x4_t c[RB][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int r = 16 * kt + j;
-      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < RB; ++b) c[b][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4_t kv =
             *reinterpret_cast<const u32x4_t*>(&lds.k[buf][r][((grp + 4 * ks) ^ (r % CH16)) * 8]);
-        c = Mma<DT>::run(kv, qb[ks], c);
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t0 + 16 * kt + 4 * grp + i;
-        lg[kt][i] = key < row_end ? c[i] * sl2 : -INFINITY;
+        for (int b = 0; b < RB; ++b) c[b][kt] = Mma<DT>::run(kv, qb[b][ks], c[b][kt]);
       }
     }
-    float mx = lg[0][0];
+    const bool nomask = t0 + kMqStep <= wmin;      // uniform
+    u32x4_t pb[RB];
+    float alpha[RB];
+    bool moved = false;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int b = 0; b < RB; ++b) {
+      float lg[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, lg[kt][i]);
-    mx = mq_max_over_groups(mx);
-    const float mn = fmaxf(st.m, mx);
-    const float alpha = fast_exp2(st.m - mn);
-    float p[8];
-    float ps = 0.f;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 4; ++i) {
+          const float x = c[b][kt][i] * sl2;
+          lg[4 * kt + i] = (nomask || t0 + 16 * kt + 4 * grp + i < row_end[b]) ? x : -INFINITY;
+        }
+      float mx = lg[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[4 * kt + i] = fast_exp2(lg[kt][i] - mn);
-        ps += p[4 * kt + i];
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
+      mx = mq_max_over_groups(mx);
+      const bool up = mx > st.m[b] + kMqSlack;
+      const float mn = up ? mx : st.m[b];
+      alpha[b] = up ? fast_exp2(st.m[b] - mn) : 1.f;
+      moved |= up;
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = fast_exp2(lg[i] - mn);
+        ps += p[i];
       }
-    st.lsum = fmaf(st.lsum, alpha, ps);
-    st.m = mn;
-    u32x4_t pb;
+      st.lsum[b] = fmaf(st.lsum[b], alpha[b], ps);
+      st.m[b] = mn;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      pb[e] = (uint32_t)S::from_float(p[2 * e]) | ((uint32_t)S::from_float(p[2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) pb[b][e] = Mma<DT>::pack(p[2 * e], p[2 * e + 1]);
+    }
+    if (__ballot(moved) != 0) {                   // uniform: some row moved its reference
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) st.acc[b][dt] *= alpha[b];
+    }
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      st.acc[dt] *= alpha;
       const uint32_t* vr = &lds.v[buf][16 * dt + j][2 * grp];
       const uint2 lo = *reinterpret_cast<const uint2*>(vr);       // keys 4g .. 4g+3
       const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);   // keys 16+4g .. 16+4g+3
-      st.acc[dt] = Mma<DT>::run(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, st.acc[dt]);
+      const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int b = 0; b < RB; ++b) st.acc[b][dt] = Mma<DT>::run(va, pb[b], st.acc[b][dt]);
     }
   };
 
-  // Steps i = 0, 1, ...: stage ring[i % 2] into LDS buffer i % 2, refill that
-  // ring slot with step i + 2, then compute step i. One barrier per step: a
-  // wave that stages step i has passed the barrier of step i - 1, which every
-  // wave reaches only after computing step i - 2 from the same buffer.
+  // Steps i = 0, 1, ...: stage ring[i % RD] into LDS buffer i % 2, refill
+  // that ring slot with step i + RD (so RD steps of loads are in flight while
+  // step i computes), then compute step i. One barrier per step: a wave that
+  // stages step i has passed the barrier of step i - 1, which every wave
+  // reaches only after computing step i - 2 from the same buffer.
   const int nsteps = kend > c0 ? (kend - c0 + kMqStep - 1) / kMqStep : 0;
-  if (nsteps > 0) issue(c0, ring[0]);
-  if (nsteps > 1) issue(c0 + kMqStep, ring[1]);
-  for (int i = 0; i < nsteps; i += 2) {
-    stage(ring[0], 0);
-    if (i + 2 < nsteps) issue(c0 + (i + 2) * kMqStep, ring[0]);
-    __syncthreads();
-    compute(c0 + i * kMqStep, 0);
-    if (i + 1 >= nsteps) break;
-    stage(ring[1], 1);
-    if (i + 3 < nsteps) issue(c0 + (i + 3) * kMqStep, ring[1]);
-    __syncthreads();
-    compute(c0 + (i + 1) * kMqStep, 1);
+#pragma unroll
+  for (int r = 0; r < RD; ++r)
+    if (r < nsteps) issue(c0 + r * kMqStep, ring[r]);
+  for (int i = 0; i < nsteps; i += RD) {
+#pragma unroll
+    for (int r = 0; r < RD; ++r) {
+      const int step = i + r;
+      if (step >= nsteps) break;                  // uniform
+      stage(ring[r], r & 1);
+      if (step + RD < nsteps) issue(c0 + (step + RD) * kMqStep, ring[r]);
+      __syncthreads();
+      compute(c0 + step * kMqStep, r & 1);
+    }
   }
   __syncthreads();   // the last step's LDS reads are done before LDS is reused
 }

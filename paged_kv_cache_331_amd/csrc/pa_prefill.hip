@@ -9,9 +9,9 @@
 // positions L - n .. L - 1. The token at position p attends to 0 .. p.
 //
 // Work decomposition: one work-group per (kv head g, sequence s, tile of
-// 64 / G new tokens): its 64 query rows are those tokens' G query heads of kv
-// head g (so each K/V row staged serves G heads), on the matrix-core core of
-// pa_mq.h. The work-group walks positions 0 .. (its last token's position)
+// 128 / G new tokens): its 128 query rows (4 waves x 2 blocks of 16) are those
+// tokens' G query heads of kv head g, so each K/V row staged serves every
+// row, on the matrix-core core of pa_mq.h. The work-group walks positions 0 .. (its last token's position)
 // in chunks of 256 table entries staged in LDS; each row masks the keys past
 // its own position. Tiles with more keys (later in a sequence) are
 // dispatched first.
@@ -23,6 +23,11 @@ namespace {
 
 constexpr int kSlotThreads = 256;
 constexpr int kTblChunk = 256;           // table entries staged per LDS pass
+#ifndef PA_PREFILL_ROW_BLOCKS
+#define PA_PREFILL_ROW_BLOCKS 1
+#endif
+constexpr int kPrefillRowBlocks = PA_PREFILL_ROW_BLOCKS;   // 16-row blocks per wave
+constexpr int kPrefillRowsPerWg = kMqWaves * kMqRowsPerBlock * kPrefillRowBlocks;
 
 // Clamped view of sequence s's new-token rows: [a, a + n).
 __device__ __forceinline__ void new_rows(const PrefillParams& p, int s, int L, int& a, int& n) {
@@ -51,7 +56,8 @@ template <class DT, int D, int G>
 __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillParams p) {
   using S = Storage<DT>;
   constexpr int NT = kMqWaves * 64;
-  constexpr int TPW = kMqRowsPerWg / G;    // new tokens per work-group
+  constexpr int RB = kPrefillRowBlocks;
+  constexpr int TPW = kPrefillRowsPerWg / G;   // new tokens per work-group
   static_assert(D == 64 || D == 128, "head size");
   __shared__ int32_t s_tbl[kTblChunk];
   __shared__ MqLds<D> lds;
@@ -73,17 +79,25 @@ __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillPar
   const int lane = tid & 63;
   const int j = lane & 15;
   const int grp = lane >> 4;
-  const int r = wave * kMqRowsPerWave + j;             // row of the work-group
-  const int ti = qt * TPW + r / G;                     // new token index in the sequence
-  const int h = g * G + r % G;
-  const bool row_ok = ti < n;
-  const int pos = L - n + ti;                          // its position
-  const int row_end = row_ok ? pos + 1 : 0;            // causal: keys 0 .. pos
   const int kend = L - n + min(n, (qt + 1) * TPW);     // one past the tile's last position
 
-  u32x4_t qb[D / 32];
-  mq_load_q<D>(qb, p.q + ((int64_t)(a + (row_ok ? ti : 0)) * p.num_q_heads + h) * D, row_ok);
-  MqState<D> st;
+  // Row block b of this wave: work-group rows wave*16*RB + 16*b + j, each a
+  // (new token, query head of kv head g) pair. Rows past the sequence's new
+  // tokens attend unmasked with q = 0 and are not written.
+  int ti[RB], h[RB], row_end[RB];
+  bool row_ok[RB];
+  u32x4_t qb[RB][D / 32];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int r = wave * kMqRowsPerBlock * RB + kMqRowsPerBlock * b + j;
+    ti[b] = qt * TPW + r / G;                          // new token index in the sequence
+    h[b] = g * G + r % G;
+    row_ok[b] = ti[b] < n;
+    row_end[b] = row_ok[b] ? L - n + ti[b] + 1 : kend; // causal: keys 0 .. its position
+    mq_load_q<D>(qb[b], p.q + ((int64_t)(a + (row_ok[b] ? ti[b] : 0)) * p.num_q_heads + h[b]) * D,
+                 row_ok[b]);
+  }
+  MqState<D, RB> st;
   st.init();
 
   const int32_t* bt_row = p.bt + (int64_t)s * p.max_blocks_per_seq;
@@ -104,29 +118,32 @@ __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillPar
       const int blk = s_tbl[(t >> lbs) - b0];
       return blk < 0 ? -1 : (int64_t)blk * bs + (t & (bs - 1));
     };
-    mq_attend<DT, D>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
-                     static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
-                     p.scale_log2, slot_of);   // ends with a barrier: s_tbl is free again
+    mq_attend<DT, D, RB>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
+                         static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
+                         p.scale_log2, slot_of);   // ends with a barrier: s_tbl is free again
   }
 
-  const float lsum = mq_sum_over_groups(st.lsum);
-  if (!row_ok) return;
-  const float inv = 1.f / lsum;
-  uint16_t* o = p.out + ((int64_t)(a + ti) * p.num_q_heads + h) * D + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    uint2 w;
-    w.x = (uint32_t)S::from_float(st.acc[dt][0] * inv) |
-          ((uint32_t)S::from_float(st.acc[dt][1] * inv) << 16);
-    w.y = (uint32_t)S::from_float(st.acc[dt][2] * inv) |
-          ((uint32_t)S::from_float(st.acc[dt][3] * inv) << 16);
-    *reinterpret_cast<uint2*>(o + 16 * dt) = w;
+  for (int b = 0; b < RB; ++b) {
+    const float lsum = mq_sum_over_groups(st.lsum[b]);
+    if (!row_ok[b]) continue;
+    const float inv = 1.f / lsum;
+    uint16_t* o = p.out + ((int64_t)(a + ti[b]) * p.num_q_heads + h[b]) * D + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      uint2 w;
+      w.x = (uint32_t)S::from_float(st.acc[b][dt][0] * inv) |
+            ((uint32_t)S::from_float(st.acc[b][dt][1] * inv) << 16);
+      w.y = (uint32_t)S::from_float(st.acc[b][dt][2] * inv) |
+            ((uint32_t)S::from_float(st.acc[b][dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(o + 16 * dt) = w;
+    }
   }
 }
 
 template <class DT, int D, int G>
 hipError_t launch_pf(const PrefillParams& p, hipStream_t st) {
-  constexpr int TPW = kMqRowsPerWg / G;
+  constexpr int TPW = kPrefillRowsPerWg / G;
   PrefillParams q = p;
   q.num_tiles = (p.max_query_len + TPW - 1) / TPW;
   const uint64_t nwg = (uint64_t)p.num_kv_heads * p.num_seqs * q.num_tiles;

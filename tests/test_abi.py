@@ -241,6 +241,7 @@ def test_cascade_workspace_arithmetic(lib):
     (dict(D=96), -4),
     (dict(ws=None, wss=0), -5),
     (dict(q=None), -1),
+    (dict(NB=0), -2),                    # a shared prefix needs a pool
 ])
 def test_cascade_validation(lib, kw, code):
     a = dict(q=16, kc=16, vc=16, bt=16, lens=16, scale=0.125, out=16, B=2, Hq=4, Hkv=4, D=128,
@@ -261,6 +262,7 @@ def test_cascade_validation(lib, kw, code):
     (dict(Hq=12, Hkv=4), -4),
     (dict(qs=None), -1),
     (dict(out=8), -4),
+    (dict(NB=0), -2),                    # new tokens live in the pool
 ])
 def test_prefill_validation(lib, kw, code):
     a = dict(q=16, kc=16, vc=16, bt=16, lens=16, qs=16, scale=0.125, out=16, B=2, T=10, mq=8,

@@ -21,9 +21,11 @@
 //    rows per instruction and non-temporal loads measured ~15% faster than
 //    half rows with ordinary loads for this gather. The q.k partials are
 //    summed inside the row with DPP; nothing crosses rows in the loop.
-//  * Each token row keeps its own running max / exp-sum / V accumulator
-//    (online softmax, exact rescaling by exp2(m_old - m_new)); rows, then
-//    waves, are merged once at the end.
+//  * Each token row keeps its own softmax reference / exp-sum / V
+//    accumulator (online softmax; the reference moves, with an exact
+//    rescale by exp2(m_old - m_new), only when a tile's max exceeds it by
+//    more than 8 in log2 units); rows, then waves, are merged once at the
+//    end.
 //  * Positions >= L inside the last tile are excluded by select: the logit
 //    becomes -inf and the V row is replaced by zeros, so whatever those slots
 //    hold (even NaN) cannot reach the result. Table entries past the last
@@ -57,6 +59,7 @@ __device__ __forceinline__ void fold_prefix(const DecodeParams& a, int64_t oh, i
 
 constexpr float kEmptyMax = -1.0e30f;  // running max before any token: finite, so
                                        // exp2(m_old - m_new) never sees inf - inf
+constexpr float kSlack = 8.f;              // lazy softmax reference: weights stay <= 2^8
 constexpr int kTile = 16;                  // tokens per wave iteration
 constexpr int kTableChunk = 256;           // table entries staged per LDS pass
 
@@ -194,29 +197,43 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) KV::widen(vr[tg], vx[tg]);
 
+      // Online softmax with a lazily moved reference: a row's m only moves
+      // when the tile's max exceeds it by more than kSlack (log2 units), so
+      // the weights 2^(s - m) stay below 2^kSlack and the accumulators are
+      // rescaled only on such tiles -- skipped by the whole wave when no row
+      // moved. sum 2^(s-m) v / sum 2^(s-m) does not depend on m.
+      float pr[G][TG], alpha[G];
+      bool moved = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float mx = lg[h][0];
 #pragma unroll
         for (int tg = 1; tg < TG; ++tg) mx = fmaxf(mx, lg[h][tg]);
-        const float mn = fmaxf(m[h], mx);
-        const float alpha = fast_exp2(m[h] - mn);
-        float pr[TG];
+        const bool up = mx > m[h] + kSlack;
+        const float mn = up ? mx : m[h];
+        alpha[h] = up ? fast_exp2(m[h] - mn) : 1.f;
+        moved |= up;
         float ps = 0.f;
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg) {
-          pr[tg] = fast_exp2(lg[h][tg] - mn);
-          ps += pr[tg];
+          pr[h][tg] = fast_exp2(lg[h][tg] - mn);
+          ps += pr[h][tg];
         }
-        l[h] = fmaf(l[h], alpha, ps);
+        l[h] = fmaf(l[h], alpha[h], ps);
         m[h] = mn;
+      }
+      if (__ballot(moved) != 0) {                  // uniform
 #pragma unroll
-        for (int d = 0; d < DL; ++d) acc[h][d] *= alpha;
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int d = 0; d < DL; ++d) acc[h][d] *= alpha[h];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-          for (int d = 0; d < DL; ++d) acc[h][d] = fmaf(pr[tg], vx[tg][d], acc[h][d]);
-      }
+          for (int d = 0; d < DL; ++d) acc[h][d] = fmaf(pr[h][tg], vx[tg][d], acc[h][d]);
     }
   }
 

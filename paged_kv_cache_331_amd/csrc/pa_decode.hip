@@ -87,6 +87,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   constexpr int LPR = D / 8;           // lanes per token row (8 dimensions per lane)
   constexpr int ROWS = 64 / LPR;       // token rows per load instruction
   constexpr int TG = kTile / ROWS;     // load instructions per tile and tensor
+  static_assert(TG % 2 == 0, "p.V pairs rows tg, tg+1");
   constexpr int DL = 8;                // dimensions held per lane
   constexpr int NT = NW * 64;
   static_assert(D == 64 || D == 128, "head size");
@@ -193,9 +194,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
           vr[tg] = ok ? vr[tg] : KV::zero();
         }
       }
-      float vx[TG][8];
+      uint32_t vw[TG][4];                        // V rows as packed QT pairs
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) KV::widen(vr[tg], vx[tg]);
+      for (int tg = 0; tg < TG; ++tg) KV::pairs(vr[tg], vw[tg]);
 
       // Online softmax with a lazily moved reference: a row's m only moves
       // when the tile's max exceeds it by more than kSlack (log2 units), so
@@ -213,27 +214,41 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
         const float mn = up ? mx : m[h];
         alpha[h] = up ? fast_exp2(m[h] - mn) : 1.f;
         moved |= up;
-        float ps = 0.f;
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          pr[h][tg] = fast_exp2(lg[h][tg] - mn);
-          ps += pr[h][tg];
-        }
-        l[h] = fmaf(l[h], alpha[h], ps);
+        for (int tg = 0; tg < TG; ++tg) pr[h][tg] = fast_exp2(lg[h][tg] - mn);
         m[h] = mn;
       }
       if (__ballot(moved) != 0) {                  // uniform
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+          l[h] *= alpha[h];
 #pragma unroll
           for (int d = 0; d < DL; ++d) acc[h][d] *= alpha[h];
+        }
       }
+      // p.V on v_dot2 over token pairs: the lane's rows tg and tg+1 hold the
+      // same 8 dimensions of two tokens, so (v_A,d, v_B,d) is one packed word
+      // and (p_A, p_B) -- the weights rounded to QT -- another; the exp-sum
+      // takes the same rounded weights (a dot2 with (1, 1)).
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int i = 0; i < TG / 2; ++i) {
+        uint32_t vlo[4], vhi[4];                   // dimension 2e / 2e+1 of tokens A, B
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg)
+        for (int e = 0; e < 4; ++e) {
+          vlo[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x05040100u);
+          vhi[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x07060302u);
+        }
 #pragma unroll
-          for (int d = 0; d < DL; ++d) acc[h][d] = fmaf(pr[h][tg], vx[tg][d], acc[h][d]);
+        for (int h = 0; h < G; ++h) {
+          const uint32_t pp = S::pack2(pr[h][2 * i], pr[h][2 * i + 1]);
+          l[h] = S::dot2(pp, S::kOnes, l[h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[h][2 * e] = S::dot2(pp, vlo[e], acc[h][2 * e]);
+            acc[h][2 * e + 1] = S::dot2(pp, vhi[e], acc[h][2 * e + 1]);
+          }
+        }
+      }
     }
   }
 

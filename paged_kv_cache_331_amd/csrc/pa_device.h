@@ -35,6 +35,13 @@ template <> struct Storage<Fp16> {
   static __device__ __forceinline__ uint16_t from_float(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
   }
+  // Two finite values rounded to nearest even and packed (lo, hi): one
+  // v_cvt_pk_f16_f32.
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static constexpr uint32_t kOnes = 0x3c003c00u;   // (1, 1)
 };
 
 template <> struct Storage<Bf16> {
@@ -53,6 +60,13 @@ template <> struct Storage<Bf16> {
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
   }
+  // Two finite values rounded to nearest even and packed (lo, hi): one
+  // v_cvt_pk_bf16_f32.
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static constexpr uint32_t kOnes = 0x3f803f80u;   // (1, 1)
 };
 
 // DPP controls (GCN/CDNA encoding).
@@ -115,6 +129,11 @@ template <class QT> struct Kv<QT, QT> {
       x[2 * e + 1] = Storage<QT>::hi(v[e]);
     }
   }
+  // The 8 dimensions as 4 packed QT pairs (dimensions 2e, 2e+1 in word e).
+  static __device__ __forceinline__ void pairs(row v, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = v[e];
+  }
   static __device__ __forceinline__ row zero() { return row{0u, 0u, 0u, 0u}; }
 };
 
@@ -156,6 +175,14 @@ template <class QT> struct Kv<QT, Fp8> {
       x[4 * w + 1] = lo[1];
       x[4 * w + 2] = hi[0];
       x[4 * w + 3] = hi[1];
+    }
+  }
+  // The 8 dimensions as 4 packed QT pairs (exact, see Fp8Pair).
+  static __device__ __forceinline__ void pairs(row v, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      w[2 * i] = Fp8Pair<QT>::template get<false>(v[i]);
+      w[2 * i + 1] = Fp8Pair<QT>::template get<true>(v[i]);
     }
   }
   static __device__ __forceinline__ row zero() { return row{0u, 0u}; }

@@ -14,13 +14,13 @@
 //    every K/V row is fetched from HBM once per step.
 //  * The partition's block-table entries are staged once into LDS; each wave
 //    reads the block id of its tile from LDS and makes it wave-uniform.
-//  * A wave walks 16-token tiles. Lanes form "token rows" of head_size / 8
-//    lanes; each lane holds 8 consecutive dimensions (16 bytes) of one token,
-//    so one load instruction reads whole 256-byte (head size 128) or
-//    128-byte (head size 64) K or V rows of 4 or 8 consecutive slots. Whole
-//    rows per instruction and non-temporal loads measured ~15% faster than
-//    half rows with ordinary loads for this gather. The q.k partials are
-//    summed inside the row with DPP; nothing crosses rows in the loop.
+//  * A wave walks 16-token tiles. Lanes form "token rows"; each lane holds
+//    16 bytes of one token (8 dimensions of a 2-byte cache, 16 of an FP8 one
+//    at head size 128), so one load instruction reads whole K or V rows of
+//    4, 8 or 16 consecutive slots. Whole rows per instruction and
+//    non-temporal loads measured ~15% faster than half rows with ordinary
+//    loads for this gather. The q.k partials are summed inside the row with
+//    DPP; nothing crosses rows in the loop.
 //  * Each token row keeps its own softmax reference / exp-sum / V
 //    accumulator (online softmax; the reference moves, with an exact
 //    rescale by exp2(m_old - m_new), only when a tile's max exceeds it by
@@ -80,15 +80,15 @@ template <class DT, class KT, int D, int G>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
                                             DecodeLds<D, G>& sm) {
   using S = Storage<DT>;
-  using KV = Kv<DT, KT>;
+  constexpr int DL = LaneDims<KT, D>::value;   // dimensions held per lane (16 bytes)
+  using KV = Kv<DT, KT, DL>;
   using elem = typename KV::elem;
   using row_t = typename KV::row;
   constexpr int NW = kDecodeWaves;
-  constexpr int LPR = D / 8;           // lanes per token row (8 dimensions per lane)
+  constexpr int LPR = D / DL;          // lanes per token row
   constexpr int ROWS = 64 / LPR;       // token rows per load instruction
   constexpr int TG = kTile / ROWS;     // load instructions per tile and tensor
   static_assert(TG % 2 == 0, "p.V pairs rows tg, tg+1");
-  constexpr int DL = 8;                // dimensions held per lane
   constexpr int NT = NW * 64;
   static_assert(D == 64 || D == 128, "head size");
 
@@ -124,21 +124,23 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   const int row = lane / LPR;
   const int col = lane % LPR;
   const int64_t tok_stride = (int64_t)Hkv * D;        // elements between slots
-  const int64_t lane_elem = row * tok_stride + (int64_t)g * D + col * 8;
+  const int64_t lane_elem = row * tok_stride + (int64_t)g * D + col * DL;
   const elem* kc = static_cast<const elem*>(a.kc);
   const elem* vc = static_cast<const elem*>(a.vc);
 
   // q slices of the G query heads of this kv head (raw storage words).
-  uint32_t qw[G][4];
+  uint32_t qw[G][DL / 2];
   {
-    const uint16_t* qs = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D + col * 8;
+    const uint16_t* qs = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D + col * DL;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      Vec16 t;
-      t.v = *reinterpret_cast<const uint4*>(qs + h * D);
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qw[h][e] = t.w[e];
-    }
+      for (int c = 0; c < DL / 8; ++c) {
+        Vec16 t;
+        t.v = *reinterpret_cast<const uint4*>(qs + h * D + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qw[h][4 * c + e] = t.w[e];
+      }
   }
 
   float m[G], l[G], acc[G][DL];
@@ -194,7 +196,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
           vr[tg] = ok ? vr[tg] : KV::zero();
         }
       }
-      uint32_t vw[TG][4];                        // V rows as packed QT pairs
+      uint32_t vw[TG][DL / 2];                   // V rows as packed QT pairs
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) KV::pairs(vr[tg], vw[tg]);
 
@@ -227,14 +229,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
         }
       }
       // p.V on v_dot2 over token pairs: the lane's rows tg and tg+1 hold the
-      // same 8 dimensions of two tokens, so (v_A,d, v_B,d) is one packed word
+      // same DL dimensions of two tokens, so (v_A,d, v_B,d) is one packed word
       // and (p_A, p_B) -- the weights rounded to QT -- another; the exp-sum
       // takes the same rounded weights (a dot2 with (1, 1)).
 #pragma unroll
       for (int i = 0; i < TG / 2; ++i) {
-        uint32_t vlo[4], vhi[4];                   // dimension 2e / 2e+1 of tokens A, B
+        uint32_t vlo[DL / 2], vhi[DL / 2];         // dimension 2e / 2e+1 of tokens A, B
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < DL / 2; ++e) {
           vlo[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x05040100u);
           vhi[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x07060302u);
         }
@@ -243,7 +245,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
           const uint32_t pp = S::pack2(pr[h][2 * i], pr[h][2 * i + 1]);
           l[h] = S::dot2(pp, S::kOnes, l[h]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < DL / 2; ++e) {
             acc[h][2 * e] = S::dot2(pp, vlo[e], acc[h][2 * e]);
             acc[h][2 * e + 1] = S::dot2(pp, vhi[e], acc[h][2 * e + 1]);
           }
@@ -276,7 +278,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_part[wave][h][col * 8 + e] = acc[h][e];
+      for (int e = 0; e < DL; ++e) s_part[wave][h][col * DL + e] = acc[h][e];
       if (col == 0) {
         s_part[wave][h][D] = m[h];
         s_part[wave][h][D + 1] = l[h];

@@ -107,12 +107,18 @@ __device__ __forceinline__ u32x2_t load_stream8(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
 
-// The slice of one cached K or V row a lane holds: 8 consecutive dimensions.
+// The slice of one cached K or V row a lane holds: DL consecutive dimensions.
 // QT is the query's type (fp16 / bf16), KT the cache element type.
-template <class QT, class KT> struct Kv;
+template <class QT, class KT, int DL> struct Kv;
+
+// Dimensions per lane: 16-byte loads throughout, so 8 dimensions of a 2-byte
+// cache and 16 of an FP8 one (8 at head size 64, where 16 would leave a token
+// row of 4 lanes and an odd number of rows per tile).
+template <class KT, int D> struct LaneDims { static constexpr int value = 8; };
+template <> struct LaneDims<Fp8, 128> { static constexpr int value = 16; };
 
 // Cache in the query's 2-byte type: 16 bytes per lane.
-template <class QT> struct Kv<QT, QT> {
+template <class QT> struct Kv<QT, QT, 8> {
   typedef uint16_t elem;
   typedef u32x4_t row;
   static __device__ __forceinline__ row load(const elem* p) { return load_stream16(p); }
@@ -122,14 +128,7 @@ template <class QT> struct Kv<QT, QT> {
     for (int e = 0; e < 4; ++e) acc = Storage<QT>::dot2(q[e], k[e], acc);
     return acc;
   }
-  static __device__ __forceinline__ void widen(row v, float (&x)[8]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = Storage<QT>::lo(v[e]);
-      x[2 * e + 1] = Storage<QT>::hi(v[e]);
-    }
-  }
-  // The 8 dimensions as 4 packed QT pairs (dimensions 2e, 2e+1 in word e).
+  // The dimensions as packed QT pairs (dimensions 2e, 2e+1 in word e).
   static __device__ __forceinline__ void pairs(row v, uint32_t (&w)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = v[e];
@@ -152,40 +151,33 @@ template <> struct Fp8Pair<Bf16> {
   }
 };
 
-// FP8 E4M3 cache: 8 bytes per lane. The tensor's scale is applied outside
-// (folded into the logit scale for K, into the output for V).
-template <class QT> struct Kv<QT, Fp8> {
+// FP8 E4M3 cache: DL codes (DL bytes) per lane, W = DL / 4 words. The
+// tensor's scale is applied outside (folded into the logit scale for K, into
+// the output for V).
+template <class QT, int DL> struct Kv<QT, Fp8, DL> {
+  static_assert(DL == 8 || DL == 16, "lane width");
+  static constexpr int W = DL / 4;
   typedef uint8_t elem;
-  typedef u32x2_t row;
-  static __device__ __forceinline__ row load(const elem* p) { return load_stream8(p); }
-  static __device__ __forceinline__ float dot(const uint32_t (&q)[4], row k, float acc) {
+  typedef uint32_t row __attribute__((ext_vector_type(W)));
+  static __device__ __forceinline__ row load(const elem* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const row*>(p));
+  }
+  static __device__ __forceinline__ float dot(const uint32_t (&q)[DL / 2], row k, float acc) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < W; ++w) {
       acc = Storage<QT>::dot2(q[2 * w], Fp8Pair<QT>::template get<false>(k[w]), acc);
       acc = Storage<QT>::dot2(q[2 * w + 1], Fp8Pair<QT>::template get<true>(k[w]), acc);
     }
     return acc;
   }
-  static __device__ __forceinline__ void widen(row v, float (&x)[8]) {
+  static __device__ __forceinline__ void pairs(row v, uint32_t (&w)[DL / 2]) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
-      x[4 * w] = lo[0];
-      x[4 * w + 1] = lo[1];
-      x[4 * w + 2] = hi[0];
-      x[4 * w + 3] = hi[1];
-    }
-  }
-  // The 8 dimensions as 4 packed QT pairs (exact, see Fp8Pair).
-  static __device__ __forceinline__ void pairs(row v, uint32_t (&w)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < W; ++i) {
       w[2 * i] = Fp8Pair<QT>::template get<false>(v[i]);
       w[2 * i + 1] = Fp8Pair<QT>::template get<true>(v[i]);
     }
   }
-  static __device__ __forceinline__ row zero() { return row{0u, 0u}; }
+  static __device__ __forceinline__ row zero() { return row{}; }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

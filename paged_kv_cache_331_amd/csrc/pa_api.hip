@@ -70,23 +70,31 @@ uint32_t sched_tag(const void* workspace) {
 }
 
 // Persistent scheduling of a split call's partition kernel (the counter in
-// the workspace head; see decode_persistent_kernel). Used when the
+// the workspace head; see decode_persistent_kernel). One counter hands out
+// about 60 tickets per microsecond, so it is used only where the items are
+// few and large enough to stay well below that: partitions of at least 1024
+// tokens and at most 8192 items. Within that, it is used when the
 // (sequence, kv head) pairs alone fill the chip (partition-major grid) and
-// the kernel is bound by memory: 2-byte caches, and FP8 caches with one query
-// head per kv head. The grid is 2 work-groups per compute unit for 2-byte
-// caches and 3 for FP8 (whose items are half the bytes). Sweeps of
+// the kernel is bound by memory: 2-byte caches, and FP8 caches with one
+// query head per kv head. The grid is 2 work-groups per compute unit for
+// 2-byte caches and 3 for FP8 (whose items are half the bytes). Sweeps of
 // 0 (one work-group per item) and 2..8 per compute unit over the decode
 // workloads: 4-6% faster for the many-sequence 2-byte and FP8 MHA batches;
-// slower for few long sequences (sequence-major grid), and for FP8 GQA,
-// where the dequantisation shared by the group makes the kernel VALU-heavy
-// and the one-per-item grid keeps more waves resident.
+// slower for few long sequences (sequence-major grid), for FP8 GQA, where
+// the dequantisation shared by the group makes the kernel VALU-heavy and the
+// one-per-item grid keeps more waves resident, and for partitions of 512
+// tokens or fewer (16384+ items: 10-50% slower).
 constexpr int kPersistWgsPerCu = 2;
 constexpr int kPersistWgsPerCuFp8 = 3;
+constexpr int kPersistMinPartition = 1024;
+constexpr int64_t kPersistMaxItems = 8192;
 
 void set_sched(pa::DecodeParams& a, void* workspace, int cus, bool fp8_cache, int group) {
   a.sched = (unsigned long long*)workspace;
   a.sched_tag = sched_tag(workspace);
-  const bool persist = !a.seq_major && (!fp8_cache || group == 1);
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
+  const bool persist = !a.seq_major && (!fp8_cache || group == 1) &&
+                       a.part_tokens >= kPersistMinPartition && items <= kPersistMaxItems;
   a.persist_grid = persist ? (fp8_cache ? kPersistWgsPerCuFp8 : kPersistWgsPerCu) * cus : 0;
 }
 

@@ -8,6 +8,8 @@ with a fixed stride. Each item is computed the same way whichever
 work-group takes it, so both schedules must give bitwise-equal outputs,
 within the oracle bar, and every call must leave the counter at zero.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -36,13 +38,21 @@ def _counter(ws: torch.Tensor) -> int:
     return int(ws[4:8].view(torch.int32).item())
 
 
-def _persistent_expected(b) -> bool:
-    """The library's choice: persistent when the (sequence, kv head) pairs fill
-    the chip and the cache is 2-byte, or FP8 with one query head per kv head."""
+def _persistent_expected(b, P: int) -> bool:
+    """The library's choice: persistent when the call splits into partitions
+    of at least 1024 tokens, at most 8192 (kv head, sequence, partition)
+    items, the (sequence, kv head) pairs fill the chip, and the cache is
+    2-byte, or FP8 with one query head per kv head."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     spec = b.spec
+    if P == 0:
+        P = pa.decode_partition_size(b.num_seqs, spec.num_kv_heads, b.max_context_len)
+    if P < 0:
+        return False
+    parts = -(-b.max_context_len // P)
     group = spec.num_q_heads // spec.num_kv_heads
-    return (b.num_seqs * spec.num_kv_heads >= cus
+    return (parts > 1 and P >= 1024 and b.num_seqs * spec.num_kv_heads * parts <= 8192
+            and b.num_seqs * spec.num_kv_heads >= cus
             and (b.cache_dtype != "fp8" or group == 1))
 
 
@@ -66,13 +76,13 @@ def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-# Batches with at least 256 (sequence, kv head) pairs take the persistent
-# schedule (except FP8 GQA); the others check that the one-per-item path
-# leaves the workspace head alone.
+# Batches of at least 256 (sequence, kv head) pairs with 1024-token partitions
+# take the persistent schedule (except FP8 GQA); the others check that the
+# one-per-item path leaves the workspace head alone.
 @pytest.mark.parametrize("name,seqs,P", [
-    ("llama2_7b_mha", 8, 64), ("gqa_8b", 32, 256), ("long_context_splitk", 1, 512),
-    ("llama2_7b_mha_fp8", 8, 128), ("gqa_8b_fp8", 32, 64), ("tiny_write", 4, 32),
-    ("llama2_7b_mha", 4, 128),
+    ("llama2_7b_mha", 8, 1024), ("gqa_8b", 32, 1024), ("llama2_7b_mha_fp8", 8, 1024),
+    ("gqa_8b_fp8", 32, 1024), ("llama2_7b_mha", 8, 256), ("long_context_splitk", 1, 512),
+    ("tiny_write", 4, 32), ("llama2_7b_mha", 4, 128),
 ])
 def test_workspace_reuse_small_all_outputs(name, seqs, P):
     spec = wl.small_variant(name, seqs)
@@ -84,7 +94,7 @@ def test_workspace_reuse_small_all_outputs(name, seqs, P):
     ws = _random_workspace(pa.decode_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size,
                                                     b.max_context_len, P), 5)
     head = ws[:8].clone()
-    persistent = _persistent_expected(b)
+    persistent = _persistent_expected(b, P)
     say(f"schedule reuse {name} B={b.num_seqs} P={P} persistent={persistent}")
     outs = [_decode(b, d, ws, P) for _ in range(3)]
     assert _head_rewritten(ws, head[:4]) == persistent
@@ -104,8 +114,8 @@ def test_workspace_shared_by_calls_of_different_shapes():
     (fixed-stride) run and the oracle."""
     b1 = wl.make_batch(wl.small_variant("gqa_8b", 40))
     b2 = wl.make_batch(wl.small_variant("llama2_7b_mha", 9))
-    assert _persistent_expected(b1) and _persistent_expected(b2)
-    P1, P2 = 64, 128
+    P1, P2 = 1024, 1024
+    assert _persistent_expected(b1, P1) and _persistent_expected(b2, P2)
     n = max(pa.decode_workspace_size(b.num_seqs, b.spec.num_q_heads, b.spec.head_size,
                                      b.max_context_len, P)
             for b, P in ((b1, P1), (b2, P2)))
@@ -140,8 +150,8 @@ def test_workspace_reuse_full_size_sampled(name):
     head = ws[:4].clone()
     say(f"schedule reuse full {name} B={b.num_seqs} maxlen={b.max_context_len}")
     outs = [_decode(b, d, ws, 0) for _ in range(3)]
-    assert _head_rewritten(ws, head) == _persistent_expected(b)
-    if _persistent_expected(b):
+    assert _head_rewritten(ws, head) == _persistent_expected(b, 0)
+    if _persistent_expected(b, 0):
         assert _counter(ws) == 0
     assert _same(outs[0], outs[1]) and _same(outs[1], outs[2])
     kc, vc, _ = oracle_caches(b, False)
@@ -160,11 +170,14 @@ def test_workspace_reuse_full_size_sampled(name):
 
 
 def test_cascade_workspace_reuse():
-    spec = wl.small_variant("prefix_shared_write", 32)
+    """Suffixes of up to 2500 tokens in 1024-token partitions: the cascade's
+    suffix kernel runs on the persistent grid and its combine resets the
+    counter."""
+    spec = dataclasses.replace(wl.CONFIGS["prefix_shared_write"], num_seqs=32, len_hi=2500)
     b = wl.make_batch(spec)
     d = Device(b)
     pfx = spec.shared_prefix_blocks
-    P = 64
+    P = 1024
     n = pa.decode_cascade_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size,
                                          spec.block_size, b.max_context_len, pfx, P)
     ws = _random_workspace(n, 11)

@@ -33,6 +33,10 @@ COMMON_FLAGS = [
     "-Wno-unused-function",
     # No packed-fp32 VALU instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in VGPRs: with AGPR accumulators every
+    # attention step copied them out for the (rarely taken) softmax rescale;
+    # prefill measured 6% faster without those copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

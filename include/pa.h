@@ -299,7 +299,8 @@ PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_h
  *                        256-byte aligned; used as pa_decode uses its workspace
  * Errors: those of pa_decode, and PA_ERR_SHAPE for shared_prefix_blocks out
  * of range or (with shared_prefix_blocks > 0 and num_seqs > 0) num_blocks
- * == 0. Caches of the query's 2-byte type only.
+ * == 0 or num_blocks * block_size above INT32_MAX (slots are int32). Caches
+ * of the query's 2-byte type only.
  */
 PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* value_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
@@ -356,7 +357,8 @@ PA_API int pa_prefill_slot_mapping(const int32_t* block_tables, int32_t max_bloc
  * [0, num_blocks) read as zeros. No workspace is needed.
  * Errors: as pa_decode (dtype, shapes, head size 64 / 128, block size
  * 16 / 32, group 1 / 2 / 4 / 8, alignment, NULL, HIP), and PA_ERR_SHAPE for
- * num_blocks == 0 when there are new tokens (they live in the pool).
+ * num_blocks == 0 when there are new tokens (they live in the pool) and for
+ * num_blocks * block_size above INT32_MAX (slots are int32).
  * num_seqs, num_tokens or max_query_len == 0 returns PA_OK.
  */
 PA_API int pa_prefill(const void* q, const void* key_cache, const void* value_cache,

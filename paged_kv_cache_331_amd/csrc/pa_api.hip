@@ -416,6 +416,7 @@ int pa_decode_cascade(const void* q, const void* key_cache, const void* value_ca
   // A shared prefix lives in the pool; the matrix-core kernel also relies on
   // slot 0 existing (a masked position reads it).
   if (num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
   if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
@@ -517,6 +518,7 @@ int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
   // New tokens were written into the pool, so it has blocks; the matrix-core
   // kernel also relies on slot 0 existing (a masked position reads it).
   if (num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
   if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start ||
       !out)
     return PA_ERR_NULL;

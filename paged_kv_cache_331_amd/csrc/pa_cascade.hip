@@ -88,9 +88,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const Dec
   mq_load_q<D>(qb[0], a.q + ((int64_t)s * a.num_q_heads + h) * D, row_ok);
   MqState<D, 1> st;
   st.init();
-  auto slot_of = [&](int t) -> int64_t {
+  auto slot_of = [&](int t) -> int {
     const int blk = s_tbl[(t >> lbs) - b0];
-    return blk < 0 ? -1 : (int64_t)blk * bs + (t & (bs - 1));
+    return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
   };
   // Rows past the batch attend unmasked with q = 0 and are not written.
   const int row_end[1] = {row_ok ? min(limit, c1) : kend};

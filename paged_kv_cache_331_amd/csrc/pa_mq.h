@@ -116,8 +116,8 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 }
 
 // Attend every row of the work-group to positions [c0, kend) of kv head g.
-// slot_of(t) gives position t's physical slot for c0 <= t < kend (or -1: a
-// skipped block, read as zeros). Keys >= row_end[b] are masked for this
+// slot_of(t) gives position t's physical slot (int32, as the slot mapping
+// defines it) for c0 <= t < kend, or -1 for a skipped block, read as zeros. Keys >= row_end[b] are masked for this
 // lane's row of block b; every position below kend must hold finite data (a
 // position some row of the work-group may use). Must be reached by all
 // threads of the work-group with the same c0 / kend (it synchronises); LDS is
@@ -143,6 +143,9 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   const bool vthread = tid < 16 * CH;          // uniform per wave
   const uint16_t* kbase = kc + (int64_t)g * D;
   const uint16_t* vbase = vc + (int64_t)g * D + vd;
+  const uint32_t stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^31 elements
+  // Element offset of a slot's row: one 32 x 32 -> 64-bit multiply.
+  auto row_off = [&](int sl) -> uint64_t { return (uint64_t)(uint32_t)sl * stride32; };
   // One ring slot: a step's loads in flight, and which of them hold a real
   // slot (bit u: K chunk u, bit KLOADS + e: V row e). The zeros replace the
   // others when the slot is staged, not at issue: using a load's result
@@ -161,8 +164,8 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   for (int o = 32; o >= 1; o >>= 1) wmin = min(wmin, __shfl_xor(wmin, o));
   wmin = __builtin_amdgcn_readfirstlane(wmin);
 
-  auto slot = [&](int t) -> int64_t {
-    const int64_t sl = slot_of(t < kend ? t : kend - 1);
+  auto slot = [&](int t) -> int {
+    const int sl = slot_of(t < kend ? t : kend - 1);
     return t < kend ? sl : -1;
   };
   auto issue = [&](int t0, Regs& rg) {
@@ -170,15 +173,15 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int idx = tid + NT * u;
-      const int64_t sl = slot(t0 + idx / CH);
-      rg.k[u] = load_stream16(kbase + (sl >= 0 ? sl : 0) * tok_stride + (idx % CH) * 8);
+      const int sl = slot(t0 + idx / CH);
+      rg.k[u] = load_stream16(kbase + row_off(sl >= 0 ? sl : 0) + (idx % CH) * 8);
       ok |= (sl >= 0 ? 1u : 0u) << u;
     }
     if (vthread) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int64_t sl = slot(t0 + 2 * kp + e);
-        rg.v[e] = load_stream16(vbase + (sl >= 0 ? sl : 0) * tok_stride);
+        const int sl = slot(t0 + 2 * kp + e);
+        rg.v[e] = load_stream16(vbase + row_off(sl >= 0 ? sl : 0));
         ok |= (sl >= 0 ? 1u : 0u) << (KLOADS + e);
       }
     }

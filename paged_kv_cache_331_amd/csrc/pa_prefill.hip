@@ -114,9 +114,9 @@ __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillPar
       s_tbl[i] = (uint64_t)(uint32_t)blk < (uint64_t)p.num_blocks ? blk : -1;
     }
     __syncthreads();
-    auto slot_of = [&](int t) -> int64_t {
+    auto slot_of = [&](int t) -> int {
       const int blk = s_tbl[(t >> lbs) - b0];
-      return blk < 0 ? -1 : (int64_t)blk * bs + (t & (bs - 1));
+      return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
     };
     mq_attend<DT, D, RB>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
                          static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,

@@ -242,6 +242,7 @@ def test_cascade_workspace_arithmetic(lib):
     (dict(ws=None, wss=0), -5),
     (dict(q=None), -1),
     (dict(NB=0), -2),                    # a shared prefix needs a pool
+    (dict(NB=2**27, bs=32), -2),         # slots beyond int32
 ])
 def test_cascade_validation(lib, kw, code):
     a = dict(q=16, kc=16, vc=16, bt=16, lens=16, scale=0.125, out=16, B=2, Hq=4, Hkv=4, D=128,
@@ -263,6 +264,7 @@ def test_cascade_validation(lib, kw, code):
     (dict(qs=None), -1),
     (dict(out=8), -4),
     (dict(NB=0), -2),                    # new tokens live in the pool
+    (dict(NB=2**27, bs=32), -2),         # slots beyond int32
 ])
 def test_prefill_validation(lib, kw, code):
     a = dict(q=16, kc=16, vc=16, bt=16, lens=16, qs=16, scale=0.125, out=16, B=2, T=10, mq=8,

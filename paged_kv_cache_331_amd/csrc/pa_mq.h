@@ -117,11 +117,11 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 
 // Attend every row of the work-group to positions [c0, kend) of kv head g.
 // slot_of(t) gives position t's physical slot (int32, as the slot mapping
-// defines it) for c0 <= t < kend, or -1 for a skipped block, read as zeros. Keys >= row_end[b] are masked for this
-// lane's row of block b; every position below kend must hold finite data (a
-// position some row of the work-group may use). Must be reached by all
-// threads of the work-group with the same c0 / kend (it synchronises); LDS is
-// free again when it returns.
+// defines it) for c0 <= t < kend, or -1 for a skipped block, read as zeros.
+// Keys >= row_end[b] are masked for this lane's row of block b; every
+// position below kend must hold finite data (a position some row of the
+// work-group may use). Must be reached by all threads of the work-group with
+// the same c0 / kend (it synchronises); LDS is free again when it returns.
 template <class DT, int D, int RB, class SlotOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
                                           MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,

@@ -2,7 +2,8 @@
 // that share a kv head, attended to a range of positions reached through a
 // block table. Used by the cascade's shared-prefix kernel and by prefill.
 //
-// A work-group is 4 wave64s; each wave owns RB blocks of 16 query rows. With
+// A work-group is W wave64s (4 by default); each wave owns RB blocks of 16
+// query rows. With
 // v_mfma_f32_16x16x32 (lane l: A row l%16, B column l%16, k = 8*(l/16)..+7;
 // C column l%16, rows 4*(l/16)..+3) one 32-key step computes, per row block,
 //   S^T(16 keys x 16 queries)   = K(16 keys x D) . Q^T(D x 16 queries)   (two key tiles)
@@ -122,12 +123,12 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 // position below kend must hold finite data (a position some row of the
 // work-group may use). Must be reached by all threads of the work-group with
 // the same c0 / kend (it synchronises); LDS is free again when it returns.
-template <class DT, int D, int RB, class SlotOf>
+template <class DT, int D, int RB, int W = kMqWaves, class SlotOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
                                           MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,
                                           int64_t tok_stride, int g, int c0, int kend,
                                           const int (&row_end)[RB], float sl2, SlotOf slot_of) {
-  constexpr int NT = kMqWaves * 64;
+  constexpr int NT = W * 64;                   // W waves of 16 * RB rows each
   constexpr int KS = D / 32;
   constexpr int DTILES = D / 16;
   constexpr int CH = D / 8;                    // 16-byte chunks of a row

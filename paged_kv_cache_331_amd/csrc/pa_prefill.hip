@@ -24,10 +24,19 @@ namespace {
 constexpr int kSlotThreads = 256;
 constexpr int kTblChunk = 256;           // table entries staged per LDS pass
 #ifndef PA_PREFILL_ROW_BLOCKS
-#define PA_PREFILL_ROW_BLOCKS 1
+#define PA_PREFILL_ROW_BLOCKS 2
 #endif
 constexpr int kPrefillRowBlocks = PA_PREFILL_ROW_BLOCKS;   // 16-row blocks per wave
-constexpr int kPrefillRowsPerWg = kMqWaves * kMqRowsPerBlock * kPrefillRowBlocks;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+// Waves per work-group: more waves share each staged K/V tile among more
+// query rows (head size 128; at 64 the K tile has too few chunks for 8).
+template <int D> struct PrefillWaves { static constexpr int value = D == 128 ? PA_PREFILL_WAVES : 4; };
+template <int D>
+constexpr int prefill_rows_per_wg() {
+  return PrefillWaves<D>::value * kMqRowsPerBlock * kPrefillRowBlocks;
+}
 
 // Clamped view of sequence s's new-token rows: [a, a + n).
 __device__ __forceinline__ void new_rows(const PrefillParams& p, int s, int L, int& a, int& n) {
@@ -53,11 +62,12 @@ __global__ __launch_bounds__(kSlotThreads) void prefill_slot_kernel(const Prefil
 }
 
 template <class DT, int D, int G>
-__global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(const PrefillParams p) {
   using S = Storage<DT>;
-  constexpr int NT = kMqWaves * 64;
+  constexpr int W = PrefillWaves<D>::value;
+  constexpr int NT = W * 64;
   constexpr int RB = kPrefillRowBlocks;
-  constexpr int TPW = kPrefillRowsPerWg / G;   // new tokens per work-group
+  constexpr int TPW = prefill_rows_per_wg<D>() / G;   // new tokens per work-group
   static_assert(D == 64 || D == 128, "head size");
   __shared__ int32_t s_tbl[kTblChunk];
   __shared__ MqLds<D> lds;
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillPar
       const int blk = s_tbl[(t >> lbs) - b0];
       return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
     };
-    mq_attend<DT, D, RB>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
+    mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
                          static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
                          p.scale_log2, slot_of);   // ends with a barrier: s_tbl is free again
   }
@@ -143,13 +153,14 @@ __global__ __launch_bounds__(kMqWaves * 64) void prefill_kernel(const PrefillPar
 
 template <class DT, int D, int G>
 hipError_t launch_pf(const PrefillParams& p, hipStream_t st) {
-  constexpr int TPW = kPrefillRowsPerWg / G;
+  constexpr int TPW = prefill_rows_per_wg<D>() / G;
   PrefillParams q = p;
   q.num_tiles = (p.max_query_len + TPW - 1) / TPW;
   const uint64_t nwg = (uint64_t)p.num_kv_heads * p.num_seqs * q.num_tiles;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), dim3((uint32_t)nwg), dim3(kMqWaves * 64), 0, st,
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), dim3((uint32_t)nwg),
+                     dim3(PrefillWaves<D>::value * 64), 0, st,
                      q);
   return hipGetLastError();
 }

@@ -124,7 +124,7 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
            "write_scale": f_write, "kernels": {}}
     total = 0.0
     for tag in ("cascade_prefix_kernel", "decode_partition_kernel", "decode_persistent_kernel",
-                "decode_reduce_kernel"):
+                "decode_reduce_kernel", "decode_reduce_few_kernel"):
         m = lambda k, tag=tag: tag in k
         try:
             fk, n = median_kib(fetch_csv, "FETCH_SIZE", m)

@@ -193,3 +193,34 @@ def test_cascade_workspace_reuse():
     ref = oracle.decode(b.q, b.key_cache, b.value_cache, b.block_tables, b.context_lens, b.scale,
                         b.dtype)
     assert max_err(outs[2], ref) <= TOL[b.dtype]
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two persistent-grid calls in flight at once on two streams, each with
+    its own workspace (the rule for concurrent calls): both match their
+    results from one stream, several times over."""
+    b1 = wl.make_batch(wl.small_variant("gqa_8b", 40))
+    b2 = wl.make_batch(wl.small_variant("llama2_7b_mha", 9))
+    P = 1024
+    assert _persistent_expected(b1, P) and _persistent_expected(b2, P)
+    d1, d2 = Device(b1), Device(b2)
+    ws = [_random_workspace(pa.decode_workspace_size(b.num_seqs, b.spec.num_q_heads,
+                                                     b.spec.head_size, b.max_context_len, P), 21 + i)
+          for i, b in enumerate((b1, b2))]
+    ref1, ref2 = _decode(b1, d1, ws[0], P), _decode(b2, d2, ws[1], P)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            o1 = pa.decode(d1.q, d1.kc, d1.vc, d1.bt, d1.lens, float(b1.scale), b1.max_context_len,
+                           partition_size=P, workspace=ws[0])
+        with torch.cuda.stream(s2):
+            o2 = pa.decode(d2.q, d2.kc, d2.vc, d2.bt, d2.lens, float(b2.scale), b2.max_context_len,
+                           partition_size=P, workspace=ws[1])
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert _same(o1, ref1) and _same(o2, ref2)
+    assert _counter(ws[0]) == 0 and _counter(ws[1]) == 0

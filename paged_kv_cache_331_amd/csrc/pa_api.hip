@@ -461,7 +461,8 @@ int pa_decode_cascade(const void* q, const void* key_cache, const void* value_ca
   a.always_combine = 0;     // one-partition suffixes fold the prefix in the partition kernel
   a.prefix_len = c.prefix_len;
   a.prefix_chunks = c.chunks;
-  a.prefix_row_tiles = (int32_t)((rows + 63) / 64);
+  const int rows_per_wg = pa::cascade_rows_per_wg(head_size);
+  a.prefix_row_tiles = (int32_t)((rows + rows_per_wg - 1) / rows_per_wg);
   set_sched(a, workspace, cus, false, group);
   const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;

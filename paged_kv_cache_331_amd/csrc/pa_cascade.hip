@@ -30,11 +30,14 @@ namespace pa {
 namespace {
 
 template <class DT, int D, int G>
-__global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const DecodeParams a) {
-  constexpr int NT = kMqWaves * 64;
+__global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(const DecodeParams a) {
+  constexpr int W = cascade_waves(D);
+  constexpr int RB = kCascadeRowBlocks;
+  constexpr int NT = W * 64;
   static_assert(D == 64 || D == 128, "head size");
+  static_assert(kMqStep * (D / 8) % NT == 0, "K staging needs whole chunks per thread");
   __shared__ int32_t s_tbl[kPrefixChunk / 16];
-  __shared__ int s_limit[kMqWaves];
+  __shared__ int s_limit[W];
   __shared__ MqLds<D> lds;
 
   const int Hkv = a.num_kv_heads;
@@ -50,22 +53,29 @@ __global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const Dec
   const int grp = lane >> 4;
 
   const int R = a.num_seqs * G;          // query rows of kv head g
-  const int r = rt * kMqWaves * kMqRowsPerBlock + wave * kMqRowsPerBlock + j;
-  const bool row_ok = r < R;
-  const int s = row_ok ? r / G : 0;
-  const int h = g * G + (row_ok ? r % G : 0);
-
   const int c0 = chunk * kPrefixChunk;
   const int c1 = min(a.prefix_len, c0 + kPrefixChunk);
-  int limit = 0;                          // keys this row may use: min(L, prefix_len)
-  if (row_ok) {
-    int L = a.lens[s];
-    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-    limit = min(L, a.prefix_len);
+  // Row block b of this wave: row rt * rows-per-work-group + wave * 16 * RB +
+  // 16 * b + j, a (sequence, query head) pair of kv head g.
+  int s[RB], h[RB], limit[RB];
+  bool row_ok[RB];
+  int wl = 0;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int r = rt * cascade_rows_per_wg(D) + wave * 16 * RB + 16 * b + j;
+    row_ok[b] = r < R;
+    s[b] = row_ok[b] ? r / G : 0;
+    h[b] = g * G + (row_ok[b] ? r % G : 0);
+    limit[b] = 0;                        // keys this row may use: min(L, prefix_len)
+    if (row_ok[b]) {
+      int L = a.lens[s[b]];
+      L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+      limit[b] = min(L, a.prefix_len);
+    }
+    wl = max(wl, limit[b]);
   }
   // The work-group's largest limit: K/V rows at or past it are not positions
   // of any of its sequences (possibly never written), so they are not read.
-  int wl = limit;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o));
   if (lane == 0) s_limit[wave] = wl;
@@ -81,37 +91,44 @@ __global__ __launch_bounds__(kMqWaves * 64) void cascade_prefix_kernel(const Dec
   __syncthreads();
   int wg_limit = s_limit[0];
 #pragma unroll
-  for (int w = 1; w < kMqWaves; ++w) wg_limit = max(wg_limit, s_limit[w]);
+  for (int w = 1; w < W; ++w) wg_limit = max(wg_limit, s_limit[w]);
   const int kend = min(c1, wg_limit);
 
-  u32x4_t qb[1][D / 32];
-  mq_load_q<D>(qb[0], a.q + ((int64_t)s * a.num_q_heads + h) * D, row_ok);
-  MqState<D, 1> st;
+  u32x4_t qb[RB][D / 32];
+  int row_end[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    mq_load_q<D>(qb[b], a.q + ((int64_t)s[b] * a.num_q_heads + h[b]) * D, row_ok[b]);
+    // Rows past the batch attend unmasked with q = 0 and are not written.
+    row_end[b] = row_ok[b] ? min(limit[b], c1) : kend;
+  }
+  MqState<D, RB> st;
   st.init();
   auto slot_of = [&](int t) -> int {
     const int blk = s_tbl[(t >> lbs) - b0];
     return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
   };
-  // Rows past the batch attend unmasked with q = 0 and are not written.
-  const int row_end[1] = {row_ok ? min(limit, c1) : kend};
-  mq_attend<DT, D, 1>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
-                      static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend, row_end,
-                      a.scale_log2, slot_of);
+  mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
+                          static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend,
+                          row_end, a.scale_log2, slot_of);
 
-  // Partial of this chunk for the row: (reference max, sum of weights,
+  // Partial of this chunk for each row: (reference max, sum of weights,
   // unnormalised O), consistent with one another whatever the reference.
-  const float lsum = mq_sum_over_groups(st.lsum[0]);
-  if (!row_ok) return;
-  const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.part_stride + chunk;
-  if (grp == 0) {
-    a.ws_m[pi] = st.m[0];
-    a.ws_l[pi] = lsum;
-  }
-  float* po = a.ws_o + pi * D + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<float4*>(po + 16 * dt) =
-        make_float4(st.acc[0][dt][0], st.acc[0][dt][1], st.acc[0][dt][2], st.acc[0][dt][3]);
+  for (int b = 0; b < RB; ++b) {
+    const float lsum = mq_sum_over_groups(st.lsum[b]);
+    if (!row_ok[b]) continue;
+    const int64_t pi = ((int64_t)s[b] * a.num_q_heads + h[b]) * a.part_stride + chunk;
+    if (grp == 0) {
+      a.ws_m[pi] = st.m[b];
+      a.ws_l[pi] = lsum;
+    }
+    float* po = a.ws_o + pi * D + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt) =
+          make_float4(st.acc[b][dt][0], st.acc[b][dt][1], st.acc[b][dt][2], st.acc[b][dt][3]);
+  }
 }
 
 template <class DT, int D, int G>
@@ -119,8 +136,8 @@ hipError_t launch_prefix(const DecodeParams& a, hipStream_t st) {
   const uint64_t nwg = (uint64_t)a.num_kv_heads * a.prefix_row_tiles * a.prefix_chunks;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((cascade_prefix_kernel<DT, D, G>), dim3((uint32_t)nwg), dim3(kMqWaves * 64), 0,
-                     st, a);
+  hipLaunchKernelGGL((cascade_prefix_kernel<DT, D, G>), dim3((uint32_t)nwg),
+                     dim3(cascade_waves(D) * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -87,8 +87,24 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int 
                           hipStream_t stream);
 hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
 
-// Keys of the shared prefix one cascade work-group covers.
-constexpr int kPrefixChunk = 128;
+// Keys of the shared prefix one cascade work-group covers, and the shape of
+// that work-group: waves, and 16-row blocks per wave.
+#ifndef PA_PREFIX_CHUNK
+#define PA_PREFIX_CHUNK 128
+#endif
+#ifndef PA_CASCADE_WAVES
+#define PA_CASCADE_WAVES 4
+#endif
+#ifndef PA_CASCADE_ROW_BLOCKS
+#define PA_CASCADE_ROW_BLOCKS 1
+#endif
+constexpr int kPrefixChunk = PA_PREFIX_CHUNK;
+constexpr int kCascadeRowBlocks = PA_CASCADE_ROW_BLOCKS;
+// At head size 64 a 32-key K tile has 256 chunks of 16 bytes: 4 waves at most.
+constexpr int cascade_waves(int head_size) { return head_size == 128 ? PA_CASCADE_WAVES : 4; }
+constexpr int cascade_rows_per_wg(int head_size) {
+  return cascade_waves(head_size) * 16 * kCascadeRowBlocks;
+}
 
 // One decode step: the partition kernel, then (num_parts > 1) the combine.
 // dtype: q / out type (0 fp16, 1 bf16); fp8_cache: the caches hold E4M3 codes.

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(c
   int row_end[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
-    mq_load_q<D>(qb[b], a.q + ((int64_t)s[b] * a.num_q_heads + h[b]) * D, row_ok[b]);
+    mq_load_q<D>(qb[b], a.q + ((int64_t)s[b] * a.num_q_heads + h[b]) * D, row_ok[b],
+                 a.scale_log2 < 0.f);
     // Rows past the batch attend unmasked with q = 0 and are not written.
     row_end[b] = row_ok[b] ? min(limit[b], c1) : kend;
   }
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(c
   };
   mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
                           static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend,
-                          row_end, a.scale_log2, slot_of);
+                          row_end, fabsf(a.scale_log2), slot_of);
 
   // Partial of this chunk for each row: (reference max, sum of weights,
   // unnormalised O), consistent with one another whatever the reference.

@@ -75,14 +75,41 @@ template <> struct Mma<Bf16> {
   }
 };
 
-// The four lanes that share a query column (lanes j, j+16, j+32, j+48).
+// The four lanes that share a query column (lanes j, j+16, j+32, j+48), on
+// the gfx950 lane swaps: v_permlane16_swap(x, x) leaves x of lanes l and
+// l ^ 16 in its two results (in some order, per lane), v_permlane32_swap(x, x)
+// those of l and l ^ 32. No LDS round trip.
+__device__ __forceinline__ void mq_pair16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void mq_pair32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// max of two logits with v_max_f32 as is: the operands come out of the
+// matrix core or the exp unit (never signalling NaNs), so the quieting that
+// fmaxf adds around values from a lane swap is not needed.
+__device__ __forceinline__ float mq_fmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float mq_max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  float a, b;
+  mq_pair16(x, a, b);
+  mq_pair32(mq_fmax(a, b), a, b);
+  return mq_fmax(a, b);
 }
 __device__ __forceinline__ float mq_sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  float a, b;
+  mq_pair16(x, a, b);
+  mq_pair32(a + b, a, b);
+  return a + b;
 }
 
 template <int D> struct MqLds {
@@ -107,13 +134,22 @@ template <int D, int RB> struct MqState {
   }
 };
 
+template <bool B> struct MqFlag { static constexpr bool value = B; };
+
 // Q^T as the B operand: this lane's query row q (D elements), k = 8*grp + 32*ks.
+// With neg set every element's sign is flipped (exact in both 2-byte types):
+// q.k * scale = (-q).k * |scale| for a negative scale, and the core takes
+// scales >= 0 only.
 template <int D>
-__device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t* q, bool ok) {
+__device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t* q, bool ok,
+                                          bool neg) {
   const int grp = (threadIdx.x & 63) >> 4;
+  const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+  for (int ks = 0; ks < D / 32; ++ks) {
     qb[ks] = ok ? *reinterpret_cast<const u32x4_t*>(q + 8 * grp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    qb[ks] ^= flip;
+  }
 }
 
 // Attend every row of the work-group to positions [c0, kend) of kv head g.
@@ -123,6 +159,8 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 // position below kend must hold finite data (a position some row of the
 // work-group may use). Must be reached by all threads of the work-group with
 // the same c0 / kend (it synchronises); LDS is free again when it returns.
+// sl2 (scale * log2 e) must be >= 0: mq_load_q folds a negative scale's sign
+// into q.
 template <class DT, int D, int RB, int W = kMqWaves, class SlotOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
                                           MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,
@@ -157,13 +195,21 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   Regs ring[RD];
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
 
-  // The wave's smallest row limit: a step entirely below it needs no mask.
-  int wmin = row_end[0];
+  // The wave's smallest row limit: a step entirely below it needs no mask;
+  // its largest: a step entirely past it adds nothing to any of its rows.
+  int wmin = row_end[0], wmax = row_end[0];
 #pragma unroll
-  for (int b = 1; b < RB; ++b) wmin = min(wmin, row_end[b]);
+  for (int b = 1; b < RB; ++b) {
+    wmin = min(wmin, row_end[b]);
+    wmax = max(wmax, row_end[b]);
+  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wmin = min(wmin, __shfl_xor(wmin, o));
+  for (int o = 32; o >= 1; o >>= 1) {
+    wmin = min(wmin, __shfl_xor(wmin, o));
+    wmax = max(wmax, __shfl_xor(wmax, o));
+  }
   wmin = __builtin_amdgcn_readfirstlane(wmin);
+  wmax = __builtin_amdgcn_readfirstlane(wmax);
 
   auto slot = [&](int t) -> int {
     const int sl = slot_of(t < kend ? t : kend - 1);
@@ -207,6 +253,7 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
     }
   };
   auto compute = [&](int t0, int buf) {
+    if (t0 >= wmax) return;                       // uniform: every key past the wave's rows
     f32x4_t c[RB][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -221,46 +268,66 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
         for (int b = 0; b < RB; ++b) c[b][kt] = Mma<DT>::run(kv, qb[b][ks], c[b][kt]);
       }
     }
-    const bool nomask = t0 + kMqStep <= wmin;      // uniform
     u32x4_t pb[RB];
-    float alpha[RB];
+    float m_old[RB];
     bool moved = false;
+    // One row block's weights. Unmasked, the scale is applied inside the
+    // exponent's argument (one fma per key) and the max is taken on the raw
+    // products: sl2 >= 0 and rounding is monotonic, so max(c) * sl2 is exactly
+    // max(c * sl2).
+    auto weights = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      float lg[8];
+      for (int b = 0; b < RB; ++b) {
+        float lg[8];
+        float mx;
+        if constexpr (kMasked) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = c[b][kt][i] * sl2;
-          lg[4 * kt + i] = (nomask || t0 + 16 * kt + 4 * grp + i < row_end[b]) ? x : -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              lg[4 * kt + i] =
+                  t0 + 16 * kt + 4 * grp + i < row_end[b] ? c[b][kt][i] * sl2 : -INFINITY;
+          mx = lg[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
+        } else {
+          mx = c[b][0][0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, c[b][i / 4][i % 4]);
+          mx *= sl2;
         }
-      float mx = lg[0];
+        mx = mq_max_over_groups(mx);
+        m_old[b] = st.m[b];
+        const float mn = mx > st.m[b] + kMqSlack ? mx : st.m[b];
+        moved |= mn != m_old[b];
+        float p[8];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
-      mx = mq_max_over_groups(mx);
-      const bool up = mx > st.m[b] + kMqSlack;
-      const float mn = up ? mx : st.m[b];
-      alpha[b] = up ? fast_exp2(st.m[b] - mn) : 1.f;
-      moved |= up;
-      float p[8];
-      float ps = 0.f;
+        for (int i = 0; i < 8; ++i)
+          p[i] = kMasked ? fast_exp2(lg[i] - mn) : fast_exp2(fmaf(c[b][i / 4][i % 4], sl2, -mn));
+        st.m[b] = mn;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(lg[i] - mn);
-        ps += p[i];
+        for (int e = 0; e < 4; ++e) pb[b][e] = Mma<DT>::pack(p[2 * e], p[2 * e + 1]);
       }
-      st.lsum[b] = fmaf(st.lsum[b], alpha[b], ps);
-      st.m[b] = mn;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pb[b][e] = Mma<DT>::pack(p[2 * e], p[2 * e + 1]);
-    }
+    };
+    if (t0 + kMqStep <= wmin)                      // uniform: no key masked for any row
+      weights(MqFlag<false>{});
+    else
+      weights(MqFlag<true>{});
     if (__ballot(moved) != 0) {                   // uniform: some row moved its reference
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
+      for (int b = 0; b < RB; ++b) {
+        const float alpha = fast_exp2(m_old[b] - st.m[b]);   // 1 where the row did not move
+        st.lsum[b] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) st.acc[b][dt] *= alpha[b];
+        for (int dt = 0; dt < DTILES; ++dt) st.acc[b][dt] *= alpha;
+      }
     }
+    // The exp-sum from the packed weights, as the product below sees them.
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.lsum[b] = Storage<DT>::dot2(pb[b][e], Storage<DT>::kOnes, st.lsum[b]);
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
       const uint32_t* vr = &lds.v[buf][16 * dt + j][2 * grp];

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(co
     row_ok[b] = ti[b] < n;
     row_end[b] = row_ok[b] ? L - n + ti[b] + 1 : kend; // causal: keys 0 .. its position
     mq_load_q<D>(qb[b], p.q + ((int64_t)(a + (row_ok[b] ? ti[b] : 0)) * p.num_q_heads + h[b]) * D,
-                 row_ok[b]);
+                 row_ok[b], p.scale_log2 < 0.f);
   }
   MqState<D, RB> st;
   st.init();
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(co
     };
     mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
                          static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
-                         p.scale_log2, slot_of);   // ends with a barrier: s_tbl is free again
+                         fabsf(p.scale_log2), slot_of);   // ends with a barrier: s_tbl is free again
   }
 
 #pragma unroll

@@ -106,6 +106,17 @@ def oracle_decode_one(b: wl.Batch, kc, vc, s, h):
                              cache_dtype=b.cache_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
 
 
+# Half an ulp of the 2-byte output type, relative: a result of magnitude x is
+# stored with an error up to HALF_ULP_REL * x on top of the path's own error.
+HALF_ULP_REL = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def excess_err(gpu_out: torch.Tensor, ref: np.ndarray, dtype: str) -> float:
+    """Largest error beyond TOL + the output's own rounding at |ref|, or <= 0."""
+    out = to_f64(gpu_out)
+    return float(np.max(np.abs(out - ref) - TOL[dtype] - HALF_ULP_REL[dtype] * np.abs(ref)))
+
+
 def max_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
     return float(np.max(np.abs(to_f64(gpu_out) - ref))) if ref.size else 0.0
 

@@ -12,7 +12,7 @@ import torch
 import oracle
 from paged_kv_cache_331_amd import pa, workloads as wl
 
-from _paged import TOL, Device, down16, max_err, oracle_caches, say
+from _paged import TOL, Device, down16, excess_err, max_err, oracle_caches, say
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,33 @@ def test_cascade_prefix_workload_small_all_outputs(P):
     err = max_err(out, ref)
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[b.dtype]
+
+
+@pytest.mark.parametrize("mult", [-1.0, 0.0, 6.0])
+def test_cascade_and_decode_scale_sign_zero_and_large(mult):
+    """Negative, zero and large scales through the cascade (whose prefix pass
+    folds a negative scale into q's sign) and the plain decode. The large
+    scale's outputs approach single V rows; that case is held to the
+    tolerance plus the output's own rounding (half an ulp at |ref|)."""
+    spec = wl.small_variant("prefix_shared_write", 6)
+    b = wl.make_batch(spec)
+    b.scale = np.float32(b.scale * mult)
+    say(f"cascade/decode scale x{mult} B={b.num_seqs}")
+    d = Device(b)
+    _write(b, d)
+    out = _cascade(b, d, 256)
+    plain = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len)
+    torch.cuda.synchronize()
+    kc, vc, _ = oracle_caches(b, True)
+    ref = oracle.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype)
+    err_c, err_p = max_err(out, ref), max_err(plain, ref)
+    say(f"  max abs err cascade {err_c:.3e} decode {err_p:.3e}")
+    if mult > 1:
+        assert excess_err(out, ref, b.dtype) <= 0
+        assert excess_err(plain, ref, b.dtype) <= 0
+    else:
+        assert err_c <= TOL[b.dtype]
+        assert err_p <= TOL[b.dtype]
 
 
 def test_cascade_prefix_workload_full_size_sampled():

@@ -11,7 +11,7 @@ import torch
 import oracle
 from paged_kv_cache_331_amd import pa, workloads as wl
 
-from _paged import TOL, down16, max_err, say, up16, up32
+from _paged import TOL, down16, excess_err, max_err, say, up16, up32
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,31 @@ def test_prefill_small_all_outputs(name, ctx, new):
     err = max_err(out, ref)
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[b.dtype]
+
+
+@pytest.mark.parametrize("mult", [-1.0, 0.0, 6.0])
+def test_prefill_scale_sign_zero_and_large(mult):
+    """A negative scale (folded into q's sign inside the kernel), a zero scale
+    (uniform weights over each row's causal keys) and a large one (the lazy
+    softmax reference moves on most steps). With the large scale the outputs
+    approach single V rows, up to about 4 in magnitude, where half an ulp of
+    bf16 alone is 0.008: that case is held to the tolerance plus the output's
+    own rounding."""
+    b = wl.make_prefill_batch(wl.PREFILL_CONFIGS["gqa_8b_chunked_prefill"], ctx=[300, 0, 17],
+                              new=[40, 130, 1])
+    b.scale = np.float32(b.scale * mult)
+    say(f"prefill scale x{mult} T={b.num_tokens}")
+    d = Dev(b)
+    _, out = _run(b, d)
+    _, kc, vc = _oracle_caches(b)
+    ref = oracle.prefill(b.q, kc, vc, b.block_tables, b.context_lens, b.query_start, b.scale,
+                         b.dtype)
+    err = max_err(out, ref)
+    say(f"  max abs err {err:.3e}")
+    if mult > 1:
+        assert excess_err(out, ref, b.dtype) <= 0
+    else:
+        assert err <= TOL[b.dtype]
 
 
 def _edge_spec(bs, D, G, dtype):

@@ -40,13 +40,13 @@ namespace pa {
 constexpr int kMqWaves = 4;
 constexpr int kMqRowsPerBlock = 16;           // query rows of one MFMA column block
 constexpr int kMqStep = 32;                   // keys per MFMA step
-constexpr int kMqVRow = kMqStep / 2 + 6;      // 32-bit key pairs per V^T row, padded
 constexpr float kMqEmptyMax = -1.0e30f;       // running max before any key (finite)
 constexpr float kMqSlack = 8.f;               // lazy reference: weights stay <= 2^8
 #ifndef PA_MQ_RING
-#define PA_MQ_RING 4
+#define PA_MQ_RING 3
 #endif
-constexpr int kMqRing = PA_MQ_RING;           // steps of K/V loads in flight (registers)
+constexpr int kMqRing = PA_MQ_RING;           // steps of K/V loads in flight
+constexpr int kMqBufs = kMqRing + 1;          // LDS tiles: those, and the step computed
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -112,10 +112,45 @@ __device__ __forceinline__ float mq_sum_over_groups(float x) {
   return a + b;
 }
 
+// K and V tiles of kMqBufs steps, row-major (key, dimension), the 16-byte
+// chunk c of key row r stored at chunk c ^ (r % 16).
 template <int D> struct MqLds {
-  alignas(16) uint16_t k[2][kMqStep][D];
-  alignas(16) uint32_t v[2][D][kMqVRow];
+  alignas(16) uint16_t k[kMqBufs][kMqStep][D];
+  alignas(16) uint16_t v[kMqBufs][kMqStep][D];
 };
+
+// Source of the loads of positions that hold no key.
+static __device__ __attribute__((aligned(16))) const uint32_t kMqZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at lds + 16 l, lds being the same for the whole wave.
+// The compiler does not see this write: the reader waits with
+// mq_wait_loads and a barrier.
+__device__ __forceinline__ void mq_lds_load16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+// Until at most N of this wave's global loads are outstanding.
+template <int N> __device__ __forceinline__ void mq_wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) char mq_lds_byte;
+typedef __attribute__((address_space(3))) u32x4_t mq_lds_u32x4;
+typedef short mq_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mq_i16x4 mq_lds_i16x4;
+__device__ __forceinline__ mq_lds_byte* mq_lds_ptr(uint32_t a) {
+  return reinterpret_cast<mq_lds_byte*>(a);
+}
+__device__ __forceinline__ u32x4_t mq_lds_read16(const mq_lds_byte* a) {
+  return *reinterpret_cast<const mq_lds_u32x4*>(a);
+}
+// ds_read_b64_tr_b16: lane l of each 16-lane group receives, for y = 0..3,
+// the 2-byte element at (address of group lane 4 y + (l % 16) / 4) +
+// 2 * (l % 4): a 4 x 16 block of 2-byte elements read row-wise, transposed.
+__device__ __forceinline__ uint2 mq_lds_read_tr16(const mq_lds_byte* a) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       reinterpret_cast<mq_lds_i16x4*>(const_cast<mq_lds_byte*>(a))));
+}
 
 // Running softmax state of one lane, per row block: its query column's
 // reference max (identical in the column's four lanes), this lane's share of
@@ -166,34 +201,55 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
                                           MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,
                                           int64_t tok_stride, int g, int c0, int kend,
                                           const int (&row_end)[RB], float sl2, SlotOf slot_of) {
-  constexpr int NT = W * 64;                   // W waves of 16 * RB rows each
   constexpr int KS = D / 32;
   constexpr int DTILES = D / 16;
   constexpr int CH = D / 8;                    // 16-byte chunks of a row
   constexpr int CH16 = CH < 16 ? CH : 16;
-  constexpr int KLOADS = kMqStep * CH / NT;    // K chunks per thread per step
-  static_assert(KLOADS >= 1 && kMqStep * CH % NT == 0, "K staging");
+  constexpr int TILE = kMqStep * D * 2;        // bytes of one K or V tile
+  constexpr int SPW = TILE / 1024 / W;         // 1 KB tile slices each wave loads
+  static_assert(SPW >= 1 && TILE % (1024 * W) == 0, "tile slices");
+  constexpr int RD = kMqRing;
+  constexpr int NB = kMqBufs;
+  constexpr int DPS = 2 * SPW;                 // LDS loads a wave issues per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15;
   const int grp = lane >> 4;
-  const int kp = tid % 16;                     // V staging: key pair, 8 dimensions
-  const int vd = (tid / 16) * 8;
-  const bool vthread = tid < 16 * CH;          // uniform per wave
   const uint16_t* kbase = kc + (int64_t)g * D;
-  const uint16_t* vbase = vc + (int64_t)g * D + vd;
+  const uint16_t* vbase = vc + (int64_t)g * D;
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(kMqZeroChunk);
   const uint32_t stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^31 elements
   // Element offset of a slot's row: one 32 x 32 -> 64-bit multiply.
   auto row_off = [&](int sl) -> uint64_t { return (uint64_t)(uint32_t)sl * stride32; };
-  // One ring slot: a step's loads in flight, and which of them hold a real
-  // slot (bit u: K chunk u, bit KLOADS + e: V row e). The zeros replace the
-  // others when the slot is staged, not at issue: using a load's result
-  // right away would make the wave wait for it there.
-  struct Regs { u32x4_t k[KLOADS]; u32x4_t v[2]; uint32_t ok; };
-  constexpr int RD = kMqRing;
-  static_assert(RD % 2 == 0, "ring depth");
-  Regs ring[RD];
-  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+
+  // LDS byte addresses. Loads: slice u of this wave covers 16-byte units
+  // 64 * (wave + W * u) + lane of a tile, i.e. key row dr[u], chunk dc[u].
+  const uint32_t k0 = (uint32_t)(uintptr_t)&lds.k[0][0][0];
+  const uint32_t v0 = (uint32_t)(uintptr_t)&lds.v[0][0][0];
+  int dr[SPW], dc[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) {
+    const int unit = 64 * (wave + W * u) + lane;
+    dr[u] = unit / CH;
+    dc[u] = (unit % CH) ^ (dr[u] % CH16);
+  }
+  // A operand of S^T: key row 16 kt + j, chunk grp + 4 ks (kt adds 16 rows).
+  const mq_lds_byte* ka[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    ka[ks] = mq_lds_ptr(k0 + (j * D + ((grp + 4 * ks) ^ (j % CH16)) * 8) * 2);
+  // A operand of O^T, transposed reads: group lane i = 4 y + q names key row
+  // 4 grp + y (second read: + 16) and dimensions 16 dt + 4 q .. + 3, and this
+  // lane receives dimension 16 dt + j of the four keys.
+  const mq_lds_byte* va_addr[DTILES];
+  {
+    const int y = j >> 2, q = j & 3, r = 4 * grp + y;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+      va_addr[dt] =
+          mq_lds_ptr(v0 + (r * D + ((2 * dt + (q >> 1)) ^ (r % CH16)) * 8 + (q & 1) * 4) * 2);
+  }
 
   // The wave's smallest row limit: a step entirely below it needs no mask;
   // its largest: a step entirely past it adds nothing to any of its rows.
@@ -211,62 +267,42 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   wmin = __builtin_amdgcn_readfirstlane(wmin);
   wmax = __builtin_amdgcn_readfirstlane(wmax);
 
-  auto slot = [&](int t) -> int {
-    const int sl = slot_of(t < kend ? t : kend - 1);
-    return t < kend ? sl : -1;
-  };
-  auto issue = [&](int t0, Regs& rg) {
-    uint32_t ok = 0;
+  // Step at t0 into LDS buffer buf; positions >= kend and skipped blocks
+  // read the zero chunk (slot_of is only asked for positions in [c0, kend)).
+  auto issue = [&](int t0, int buf) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int idx = tid + NT * u;
-      const int sl = slot(t0 + idx / CH);
-      rg.k[u] = load_stream16(kbase + row_off(sl >= 0 ? sl : 0) + (idx % CH) * 8);
-      ok |= (sl >= 0 ? 1u : 0u) << u;
-    }
-    if (vthread) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int sl = slot(t0 + 2 * kp + e);
-        rg.v[e] = load_stream16(vbase + row_off(sl >= 0 ? sl : 0));
-        ok |= (sl >= 0 ? 1u : 0u) << (KLOADS + e);
-      }
-    }
-    rg.ok = ok;
-  };
-  auto stage = [&](const Regs& rg, int buf) {
-#pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int idx = tid + NT * u;
-      const int r = idx / CH, c = idx % CH;
-      *reinterpret_cast<u32x4_t*>(&lds.k[buf][r][(c ^ (r % CH16)) * 8]) =
-          (rg.ok >> u) & 1u ? rg.k[u] : zero;
-    }
-    if (vthread) {
-      const u32x4_t v0 = (rg.ok >> KLOADS) & 1u ? rg.v[0] : zero;
-      const u32x4_t v1 = (rg.ok >> (KLOADS + 1)) & 1u ? rg.v[1] : zero;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lds.v[buf][vd + 2 * e][kp] = (v0[e] & 0xffffu) | (v1[e] << 16);
-        lds.v[buf][vd + 2 * e + 1][kp] = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
-      }
+    for (int u = 0; u < SPW; ++u) {
+      const int t = t0 + dr[u];
+      const int sl = t < kend ? slot_of(max(min(t, kend - 1), c0)) : -1;
+      const uint64_t off = row_off(sl >= 0 ? sl : 0) + dc[u] * 8;
+      const uint32_t dst = (uint32_t)(wave + W * u) * 1024 + (uint32_t)buf * TILE;
+      mq_lds_load16(sl >= 0 ? kbase + off : zero, k0 + dst);
+      mq_lds_load16(sl >= 0 ? vbase + off : zero, v0 + dst);
     }
   };
   auto compute = [&](int t0, int buf) {
     if (t0 >= wmax) return;                       // uniform: every key past the wave's rows
+    const int bo = buf * TILE;
     f32x4_t c[RB][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int r = 16 * kt + j;
 #pragma unroll
       for (int b = 0; b < RB; ++b) c[b][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t kv =
-            *reinterpret_cast<const u32x4_t*>(&lds.k[buf][r][((grp + 4 * ks) ^ (r % CH16)) * 8]);
+        const u32x4_t kv = mq_lds_read16(ka[ks] + bo + kt * 16 * D * 2);
 #pragma unroll
         for (int b = 0; b < RB; ++b) c[b][kt] = Mma<DT>::run(kv, qb[b][ks], c[b][kt]);
       }
+    }
+    // V^T fragments of every dimension tile, read before the softmax so the
+    // LDS latency hides behind it: keys 4g .. 4g+3, then 16+4g .. 16+4g+3.
+    u32x4_t va[DTILES];
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) {
+      const uint2 lo = mq_lds_read_tr16(va_addr[dt] + bo);
+      const uint2 hi = mq_lds_read_tr16(va_addr[dt] + bo + 16 * D * 2);
+      va[dt] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
     }
     u32x4_t pb[RB];
     float m_old[RB];
@@ -329,37 +365,32 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.lsum[b] = Storage<DT>::dot2(pb[b][e], Storage<DT>::kOnes, st.lsum[b]);
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      const uint32_t* vr = &lds.v[buf][16 * dt + j][2 * grp];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr);       // keys 4g .. 4g+3
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);   // keys 16+4g .. 16+4g+3
-      const u32x4_t va = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
-      for (int b = 0; b < RB; ++b) st.acc[b][dt] = Mma<DT>::run(va, pb[b], st.acc[b][dt]);
-    }
+      for (int b = 0; b < RB; ++b) st.acc[b][dt] = Mma<DT>::run(va[dt], pb[b], st.acc[b][dt]);
   };
 
-  // Steps i = 0, 1, ...: stage ring[i % RD] into LDS buffer i % 2, refill
-  // that ring slot with step i + RD (so RD steps of loads are in flight while
-  // step i computes), then compute step i. One barrier per step: a wave that
-  // stages step i has passed the barrier of step i - 1, which every wave
-  // reaches only after computing step i - 2 from the same buffer.
+  // Step i lives in LDS buffer i % NB. Steps i + 1 .. i + RD - 1 are in
+  // flight while step i computes; after it, step i + RD goes into the buffer
+  // of step i - 1, which every wave finished before the barrier of step i.
+  // Steps past the range load zeros and are never computed, so the count of
+  // loads in flight is the same at every step.
   const int nsteps = kend > c0 ? (kend - c0 + kMqStep - 1) / kMqStep : 0;
 #pragma unroll
-  for (int r = 0; r < RD; ++r)
-    if (r < nsteps) issue(c0 + r * kMqStep, ring[r]);
-  for (int i = 0; i < nsteps; i += RD) {
+  for (int r = 0; r < RD; ++r) issue(c0 + r * kMqStep, r);
+  for (int i = 0; i < nsteps; i += NB) {
 #pragma unroll
-    for (int r = 0; r < RD; ++r) {
+    for (int r = 0; r < NB; ++r) {
       const int step = i + r;
       if (step >= nsteps) break;                  // uniform
-      stage(ring[r], r & 1);
-      if (step + RD < nsteps) issue(c0 + (step + RD) * kMqStep, ring[r]);
-      __syncthreads();
-      compute(c0 + step * kMqStep, r & 1);
+      mq_wait_loads<(RD - 1) * DPS>();            // this wave's loads of this step
+      __syncthreads();                            // everyone's
+      compute(c0 + step * kMqStep, r);
+      issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
     }
   }
-  __syncthreads();   // the last step's LDS reads are done before LDS is reused
+  mq_wait_loads<0>();
+  __syncthreads();   // the last loads have landed and every read is done: LDS is free
 }
 
 }  // namespace pa

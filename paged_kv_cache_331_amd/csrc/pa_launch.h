@@ -93,14 +93,14 @@ hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
 #define PA_PREFIX_CHUNK 128
 #endif
 #ifndef PA_CASCADE_WAVES
-#define PA_CASCADE_WAVES 4
+#define PA_CASCADE_WAVES 8
 #endif
 #ifndef PA_CASCADE_ROW_BLOCKS
 #define PA_CASCADE_ROW_BLOCKS 1
 #endif
 constexpr int kPrefixChunk = PA_PREFIX_CHUNK;
 constexpr int kCascadeRowBlocks = PA_CASCADE_ROW_BLOCKS;
-// At head size 64 a 32-key K tile has 256 chunks of 16 bytes: 4 waves at most.
+// At head size 64 a 32-key K tile is 4 KB, four 1 KB wave loads: 4 waves at most.
 constexpr int cascade_waves(int head_size) { return head_size == 128 ? PA_CASCADE_WAVES : 4; }
 constexpr int cascade_rows_per_wg(int head_size) {
   return cascade_waves(head_size) * 16 * kCascadeRowBlocks;

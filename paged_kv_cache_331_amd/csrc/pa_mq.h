@@ -24,13 +24,15 @@
 // does not depend on m, so this is exact up to rounding. Steps whose keys lie
 // below every row's limit in the wave skip the masking.
 //
-// Memory: each step's K and V rows are read once per work-group with
-// coalesced 16-byte loads, two steps ahead of their use, into a
-// double-buffered LDS area: K row-major with the 16-byte chunk c of key row r
-// at chunk c ^ (r % 16) (the A-operand reads then spread over all banks), V
-// transposed as one 32-bit word per (dimension, key pair) in padded rows.
-// Loads never branch: a position with no slot reads slot 0, and zeros replace
-// it when it is staged.
+// Memory: each step's K and V tiles (32 keys x D, 2-byte) go from global
+// memory straight into LDS (global_load_lds_dwordx4, no registers), read
+// once per work-group, kMqRing steps ahead of their use, into a ring of
+// kMqRing + 1 LDS buffers. Both tiles are row-major with the 16-byte chunk c
+// of key row r at chunk c ^ (r % 16): a wave's load fills 1 KB of a tile,
+// each lane fetching the chunk that lands at its 16 bytes, and both the
+// A-operand reads of K and the transposed reads of V (ds_read_b64_tr_b16,
+// which hand each lane one dimension of four keys) spread over the banks.
+// A position with no slot loads a zero chunk.
 #pragma once
 
 #include "pa_device.h"
@@ -43,7 +45,7 @@ constexpr int kMqStep = 32;                   // keys per MFMA step
 constexpr float kMqEmptyMax = -1.0e30f;       // running max before any key (finite)
 constexpr float kMqSlack = 8.f;               // lazy reference: weights stay <= 2^8
 #ifndef PA_MQ_RING
-#define PA_MQ_RING 3
+#define PA_MQ_RING 2
 #endif
 constexpr int kMqRing = PA_MQ_RING;           // steps of K/V loads in flight
 constexpr int kMqBufs = kMqRing + 1;          // LDS tiles: those, and the step computed

@@ -28,10 +28,11 @@ constexpr int kTblChunk = 256;           // table entries staged per LDS pass
 #endif
 constexpr int kPrefillRowBlocks = PA_PREFILL_ROW_BLOCKS;   // 16-row blocks per wave
 #ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
+#define PA_PREFILL_WAVES 4
 #endif
-// Waves per work-group: more waves share each staged K/V tile among more
-// query rows (head size 128; at 64 the K tile has too few chunks for 8).
+// Waves per work-group at head size 128 (at 64 the 4 KB K tile is four 1 KB
+// wave loads: 4 waves). Four waves of two row blocks leave room for two
+// work-groups per CU, whose barriers do not hold each other up.
 template <int D> struct PrefillWaves { static constexpr int value = D == 128 ? PA_PREFILL_WAVES : 4; };
 template <int D>
 constexpr int prefill_rows_per_wg() {

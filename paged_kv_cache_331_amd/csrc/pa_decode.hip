@@ -254,35 +254,69 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
     }
   }
 
-  // Merge the token rows of each wave (lanes with equal col hold equal dims).
+  // Merge the token rows of each wave: the R = 64 / LPR lanes col + LPR * r
+  // hold the same dimensions. The max and exp-sum of each head reach every
+  // lane (lane swaps for lane bits 5 and 4, a DPP rotate for bit 3). The
+  // G x DL rescaled sums are reduce-scattered instead: each step keeps half
+  // of the values, adding the partner's copy of that half, and leaves the
+  // other half to the partner, so lane (row, col) ends with the totals of
+  // values row * n .. row * n + n - 1 (value h * DL + d), n = G * DL / R.
+  static_assert(LPR == 8 || LPR == 16, "row lanes");
+  constexpr int N = G * DL;
+  constexpr int n = LPR == 8 ? N / 8 : N / 4;
+  float Mh[G], Lh[G], v[N];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = m[h];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float x = m[h], y = m[h];
+    lane_swap32(x, y);
+    float M = fmaxf(x, y);
+    x = y = M;
+    lane_swap16(x, y);
+    M = fmaxf(x, y);
+    if (LPR == 8) M = fmaxf(M, dpp<kDppRowRor8>(M));
     const float c = fast_exp2(m[h] - M);
     float lw = l[h] * c;
+    x = y = lw;
+    lane_swap32(x, y);
+    lw = x + y;
+    x = y = lw;
+    lane_swap16(x, y);
+    lw = x + y;
+    if (LPR == 8) lw += dpp<kDppRowRor8>(lw);
+    Mh[h] = M;
+    Lh[h] = lw;
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) lw += __shfl_xor(lw, o);
-#pragma unroll
-    for (int d = 0; d < DL; ++d) {
-      float x = acc[h][d] * c;
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) x += __shfl_xor(x, o);
-      acc[h][d] = x;
-    }
-    m[h] = M;
-    l[h] = lw;
+    for (int d = 0; d < DL; ++d) v[h * DL + d] = acc[h][d] * c;
   }
-  if (row == 0) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {              // lane bit 5
+    lane_swap32(v[i], v[i + N / 2]);
+    v[i] += v[i + N / 2];
+  }
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {              // lane bit 4
+    lane_swap16(v[i], v[i + N / 4]);
+    v[i] += v[i + N / 4];
+  }
+  if constexpr (LPR == 8) {                       // lane bit 3
+    const bool hi = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const float keep = hi ? v[i + N / 8] : v[i];
+      const float send = hi ? v[i] : v[i + N / 8];
+      v[i] = keep + dpp<kDppRowRor8>(send);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    const int idx = row * n + i;
+    s_part[wave][idx / DL][col * DL + idx % DL] = v[i];
+  }
+  if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < DL; ++e) s_part[wave][h][col * DL + e] = acc[h][e];
-      if (col == 0) {
-        s_part[wave][h][D] = m[h];
-        s_part[wave][h][D + 1] = l[h];
-      }
+      s_part[wave][h][D] = Mh[h];
+      s_part[wave][h][D + 1] = Lh[h];
     }
   }
   __syncthreads();

@@ -74,6 +74,7 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <-> 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // row_mirror: lane i <-> 15-i within 16 lanes
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8: lane i <-> i ^ 8 within 16 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -93,6 +94,25 @@ __device__ __forceinline__ float row_sum(float x) {
   x += dpp<kDppHalfMirror>(x);
   if (LANES == 16) x += dpp<kDppMirror>(x);
   return x;
+}
+
+// gfx950 lane swaps on a pair (a, b) holding one value per lane each:
+// lane_swap32 trades lanes 32-63 of a with lanes 0-31 of b, lane_swap16 the
+// odd 16-lane rows of a with the even rows of b. Afterwards a lane whose bit
+// 5 (resp. 4) is clear holds (its own a, its partner's a) and a lane whose
+// bit is set holds (its partner's b, its own b), the partner being lane ^ 32
+// (resp. ^ 16). With a == b both lanes see both values.
+__device__ __forceinline__ void lane_swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void lane_swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));

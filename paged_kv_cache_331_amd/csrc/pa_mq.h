@@ -27,12 +27,14 @@
 // Memory: each step's K and V tiles (32 keys x D, 2-byte) go from global
 // memory straight into LDS (global_load_lds_dwordx4, no registers), read
 // once per work-group, kMqRing steps ahead of their use, into a ring of
-// kMqRing + 1 LDS buffers. Both tiles are row-major with the 16-byte chunk c
-// of key row r at chunk c ^ (r % 16): a wave's load fills 1 KB of a tile,
-// each lane fetching the chunk that lands at its 16 bytes, and both the
-// A-operand reads of K and the transposed reads of V (ds_read_b64_tr_b16,
-// which hand each lane one dimension of four keys) spread over the banks.
-// A position with no slot loads a zero chunk.
+// kMqRing + 1 LDS buffers. Both tiles are row-major and swizzled so that
+// their reads spread over the banks: in K the 16-byte chunk c of key row r
+// sits at chunk c ^ (r % 16) (A-operand reads, 16 rows per pass), in V the
+// 32-byte unit u at u ^ (r % 8) at head size 128 (transposed reads,
+// ds_read_b64_tr_b16, which hand each lane one dimension of four keys, 8
+// rows per pass). A wave's load fills 1 KB of a tile, each lane fetching the
+// chunk that lands at its 16 bytes. A position with no slot loads a zero
+// chunk.
 #pragma once
 
 #include "pa_device.h"
@@ -114,8 +116,8 @@ __device__ __forceinline__ float mq_sum_over_groups(float x) {
   return a + b;
 }
 
-// K and V tiles of kMqBufs steps, row-major (key, dimension), the 16-byte
-// chunk c of key row r stored at chunk c ^ (r % 16).
+// K and V tiles of kMqBufs steps, row-major (key, dimension), swizzled as
+// described above.
 template <int D> struct MqLds {
   alignas(16) uint16_t k[kMqBufs][kMqStep][D];
   alignas(16) uint16_t v[kMqBufs][kMqStep][D];
@@ -229,12 +231,20 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   // 64 * (wave + W * u) + lane of a tile, i.e. key row dr[u], chunk dc[u].
   const uint32_t k0 = (uint32_t)(uintptr_t)&lds.k[0][0][0];
   const uint32_t v0 = (uint32_t)(uintptr_t)&lds.v[0][0][0];
-  int dr[SPW], dc[SPW];
+  // The V tile swizzles 32-byte units (16 dimensions) instead: unit u of key
+  // row r sits at u ^ vsw(r), so the 8 rows that half a wave's transposed
+  // read touches fall on all 64 banks.
+  constexpr int VU = D / 16;                   // 32-byte units per row
+  constexpr int RPB = 128 / D;                 // rows per 256 bytes (one pass over the banks)
+  auto vsw = [](int r) { return (r / RPB) % VU; };
+  int dr[SPW], dc[SPW], dcv[SPW];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int unit = 64 * (wave + W * u) + lane;
+    const int cp = unit % CH;
     dr[u] = unit / CH;
-    dc[u] = (unit % CH) ^ (dr[u] % CH16);
+    dc[u] = cp ^ (dr[u] % CH16);
+    dcv[u] = 2 * ((cp >> 1) ^ vsw(dr[u])) + (cp & 1);
   }
   // A operand of S^T: key row 16 kt + j, chunk grp + 4 ks (kt adds 16 rows).
   const mq_lds_byte* ka[KS];
@@ -249,8 +259,7 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
     const int y = j >> 2, q = j & 3, r = 4 * grp + y;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
-      va_addr[dt] =
-          mq_lds_ptr(v0 + (r * D + ((2 * dt + (q >> 1)) ^ (r % CH16)) * 8 + (q & 1) * 4) * 2);
+      va_addr[dt] = mq_lds_ptr(v0 + (r * D + (dt ^ vsw(r)) * 16 + q * 4) * 2);
   }
 
   // The wave's smallest row limit: a step entirely below it needs no mask;
@@ -276,10 +285,10 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
     for (int u = 0; u < SPW; ++u) {
       const int t = t0 + dr[u];
       const int sl = t < kend ? slot_of(max(min(t, kend - 1), c0)) : -1;
-      const uint64_t off = row_off(sl >= 0 ? sl : 0) + dc[u] * 8;
+      const uint64_t off = row_off(sl >= 0 ? sl : 0);
       const uint32_t dst = (uint32_t)(wave + W * u) * 1024 + (uint32_t)buf * TILE;
-      mq_lds_load16(sl >= 0 ? kbase + off : zero, k0 + dst);
-      mq_lds_load16(sl >= 0 ? vbase + off : zero, v0 + dst);
+      mq_lds_load16(sl >= 0 ? kbase + off + dc[u] * 8 : zero, k0 + dst);
+      mq_lds_load16(sl >= 0 ? vbase + off + dcv[u] * 8 : zero, v0 + dst);
     }
   };
   auto compute = [&](int t0, int buf) {

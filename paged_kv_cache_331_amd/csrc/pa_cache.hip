@@ -29,23 +29,33 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
   slots[s] = slot;
 }
 
-// One thread per 16-byte chunk of a token's [Hkv, D] row, for k and v alike.
-// row_elems = Hkv * D (a multiple of 8), so each chunk is one aligned uint4.
+// A work-group copies whole token rows: cpt = min(chunks, 256) threads per
+// token (chunks = the 16-byte chunks of a token's [Hkv, D] row, row_elems =
+// Hkv * D a multiple of 8), tpw = 256 / cpt tokens per work-group, each
+// thread striding over its token's chunks for k and v alike.
 __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kc,
     uint16_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens,
     int64_t num_slots, int32_t row_elems) {
   const int chunks = row_elems / 8;
-  const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
-  const int64_t tok = gid / chunks;
+  const int cpt = chunks < kWriteThreads ? chunks : kWriteThreads;
+  const int tpw = kWriteThreads / cpt;
+  const int lt = (int)threadIdx.x / cpt;
+  if (lt >= tpw) return;
+  const int64_t tok = (int64_t)blockIdx.x * tpw + lt;
   if (tok >= num_tokens) return;
-  const int c = (int)(gid - tok * chunks);
   const int32_t slot = slots[tok];
   if (slot < 0 || (int64_t)slot >= num_slots) return;
-  const int64_t src = tok * row_elems + (int64_t)c * 8;
-  const int64_t dst = (int64_t)slot * row_elems + (int64_t)c * 8;
-  *reinterpret_cast<uint4*>(kc + dst) = *reinterpret_cast<const uint4*>(k + src);
-  *reinterpret_cast<uint4*>(vc + dst) = *reinterpret_cast<const uint4*>(v + src);
+  const uint4* ks = reinterpret_cast<const uint4*>(k + tok * row_elems);
+  const uint4* vs = reinterpret_cast<const uint4*>(v + tok * row_elems);
+  uint4* kd = reinterpret_cast<uint4*>(kc + (int64_t)slot * row_elems);
+  uint4* vd = reinterpret_cast<uint4*>(vc + (int64_t)slot * row_elems);
+#pragma unroll 2
+  for (int c = (int)threadIdx.x - lt * cpt; c < chunks; c += cpt) {
+    const uint4 a = ks[c], b = vs[c];
+    kd[c] = a;
+    vd[c] = b;
+  }
 }
 
 // Eight 2-byte source values -> eight E4M3 codes (two words, lowest
@@ -152,8 +162,9 @@ hipError_t launch_cache_write(const uint16_t* k, const uint16_t* v, uint16_t* kc
                               const int32_t* slots, int32_t num_tokens, int64_t num_slots,
                               int32_t row_elems, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int64_t total = (int64_t)num_tokens * (row_elems / 8);
-  const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
+  const int chunks = row_elems / 8;
+  const int tpw = chunks < kWriteThreads ? kWriteThreads / chunks : 1;
+  const int64_t grid = ((int64_t)num_tokens + tpw - 1) / tpw;
   if (grid > 0x7fffffffll) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(cache_write_kernel, dim3((uint32_t)grid), dim3(kWriteThreads), 0, stream, k, v,
                      kc, vc, slots, num_tokens, num_slots, row_elems);

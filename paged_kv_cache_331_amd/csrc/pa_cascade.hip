@@ -17,8 +17,9 @@
 // reformulation, up to fp32 rounding and the 2-byte rounding of the
 // softmax weights fed to the matrix cores).
 //
-// Prefix kernel layout: one work-group (4 waves x 16 query rows) per (kv
-// head, tile of 64 rows, chunk of 128 prefix keys), on the matrix-core
+// Prefix kernel layout: one work-group (cascade_waves(D) waves of
+// kCascadeRowBlocks 16-row blocks: 8 x 1 at head size 128, 4 x 1 at 64) per
+// (kv head, row tile, chunk of kPrefixChunk prefix keys), on the matrix-core
 // attention core of pa_mq.h. Rows are (sequence, query head) pairs of the kv
 // head; each row's keys end at min(L, prefix_len), and the work-group writes
 // a (max, exp-sum, unnormalised O) partial per row for its chunk.
@@ -35,7 +36,6 @@ __global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(c
   constexpr int RB = kCascadeRowBlocks;
   constexpr int NT = W * 64;
   static_assert(D == 64 || D == 128, "head size");
-  static_assert(kMqStep * (D / 8) % NT == 0, "K staging needs whole chunks per thread");
   __shared__ int32_t s_tbl[kPrefixChunk / 16];
   __shared__ int s_limit[W];
   __shared__ MqLds<D> lds;

@@ -77,6 +77,11 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_key(workload: str, separate: bool) -> str:
+    """Key of a traffic record: the workload, and which form of the step ran."""
+    return workload + (":separate" if separate else "")
+
+
 def load_traffic(workload: str):
     """Counter-measured HBM traffic per decode call, if taken on this kernel source."""
     try:
@@ -344,6 +349,9 @@ def main(argv=None) -> int:
                     help="0 automatic, <0 single pass, >0 split-K partition tokens")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as three calls (slot mapping, cache write, decode) "
+                         "instead of one pa_decode_append call")
     ap.add_argument("--no-cascade", action="store_true",
                     help="decode a shared-prefix batch with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--copy-probe", action="store_true",
@@ -353,7 +361,8 @@ def main(argv=None) -> int:
                          "CSVs (no GPU needed)")
     args = ap.parse_args(argv)
     if args.ingest_pmc:
-        print(json.dumps(ingest_pmc(args.workload, *args.ingest_pmc), indent=1))
+        print(json.dumps(ingest_pmc(traffic_key(args.workload, args.separate), *args.ingest_pmc),
+                         indent=1))
         return 0
 
     if args.gpus != 1:
@@ -412,7 +421,26 @@ def main(argv=None) -> int:
     scale = float(batch.scale)
     stream = torch.cuda.current_stream()
 
+    fused = not args.separate
+    prefix_blocks = spec.shared_prefix_blocks if cascade else 0
+
     def step(ev0=None, ev1=None):
+        if fused:
+            # The whole step in one call: slots, the new rows stored, attention.
+            if ev0 is not None:
+                ev0.record(stream)
+            if fp8:
+                pa.decode_append_fp8(q, k_new, v_new, kc, vc, bt, lens, scale, ks, vs, maxlen,
+                                     out=out, slot_mapping=slots,
+                                     partition_size=args.partition_size, workspace=ws,
+                                     stream=stream)
+            else:
+                pa.decode_append(q, k_new, v_new, kc, vc, bt, lens, scale, maxlen, prefix_blocks,
+                                 out=out, slot_mapping=slots, partition_size=args.partition_size,
+                                 workspace=ws, stream=stream)
+            if ev1 is not None:
+                ev1.record(stream)
+            return
         pa.decode_slot_mapping(bt, lens, spec.block_size, out=slots, stream=stream)
         if fp8:
             pa.cache_write_fp8(k_new, v_new, kc, vc, slots, ks, vs, stream=stream)
@@ -458,9 +486,15 @@ def main(argv=None) -> int:
     # A block shared by many tables must come from HBM at least once, so the
     # roofline counts the shared prefix once; the per-sequence (logical)
     # rate is reported beside it.
-    achieved = nbytes["total_unique"] / (decode_ms * 1e-3) / 1e9
-    logical = nbytes["total"] / (decode_ms * 1e-3) / 1e9
-    traffic = load_traffic(spec.name)
+    # The one-call step also reads the new k/v rows, stores them and writes
+    # the slots: those bytes join the timed call's numerator.
+    app = 0
+    if fused:
+        kv_esz = 1 if fp8 else 2
+        app = batch.num_seqs * (2 * spec.num_kv_heads * spec.head_size * (2 + kv_esz) + 4)
+    achieved = (nbytes["total_unique"] + app) / (decode_ms * 1e-3) / 1e9
+    logical = (nbytes["total"] + app) / (decode_ms * 1e-3) / 1e9
+    traffic = load_traffic(traffic_key(spec.name, args.separate))
     tokens_per_s = batch.num_seqs / (ms_per_step * 1e-3)
 
     base = None
@@ -490,16 +524,20 @@ def main(argv=None) -> int:
             "partition_tokens_used": (args.partition_size if args.partition_size != 0 else
                                       pa.decode_partition_size(batch.num_seqs, spec.num_kv_heads,
                                                                maxlen)),
-            "step": "slot mapping + cache write + " + ("cascade decode (shared prefix)"
-                                                       if cascade else "decode"),
+            "step": ("one call (pa_decode_append" + ("_fp8" if fp8 else "") + "): slot mapping + "
+                     "cache write + " if fused else "slot mapping + cache write + ") +
+                    ("cascade decode (shared prefix)" if cascade else "decode"),
             "parallelism": "single GPU"},
         "roofline": {
-            "bound": "hbm", "kernel": "pa_decode (events around the call on its stream)",
+            "bound": "hbm",
+            "kernel": ("decode with append" if fused else "pa_decode") +
+                      " (events around the call on its stream)",
             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes["total_unique"],
-            "logical_bytes_per_launch": nbytes["total"], "logical_GBs": logical,
+            "algorithmic_bytes_per_launch": nbytes["total_unique"] + app,
+            "append_bytes_per_launch": app,
+            "logical_bytes_per_launch": nbytes["total"] + app, "logical_GBs": logical,
             "bytes_per_token_per_kv_head": nbytes["per_token_head"],
             "decode_ms_mean": decode_ms, "decode_ms_median": float(np.median(dec_ms)),
             "decode_ms_min": float(np.min(dec_ms)),

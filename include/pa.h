@@ -312,6 +312,65 @@ PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* v
                              size_t workspace_size, void* stream);
 
 /*
+ * pa_decode_append -- one whole decode step in one call: the slot of each
+ * sequence's new token, its k/v stored into the caches, then attention.
+ *
+ * The decode phase of "01. PagedAttention 详解" §4 computes the new token's
+ * q, k, v, appends k/v at the next slot of the sequence's last block, and
+ * attends over every cached position including the new one. With
+ * L = context_lens[s] counting the new token (it sits at position L - 1),
+ * this call has exactly the effect of
+ *   pa_decode_slot_mapping(block_tables, ..., slot_mapping);
+ *   pa_cache_write(k, v, key_cache, value_cache, slot_mapping, num_seqs, ...);
+ *   pa_decode_cascade(q, key_cache, value_cache, ..., shared_prefix_blocks, ...);
+ * (pa_decode when shared_prefix_blocks == 0): the same cache contents and the
+ * same output bits, with no separate slot or write launch. The work-group
+ * that attends over position L - 1 of kv head g stores that head's k/v row
+ * at the slot and uses the stored value as the row of that position.
+ * k, v         : [num_seqs, num_kv_heads, head_size] (device), dtype of q,
+ *                16-byte aligned
+ * slot_mapping : int32 [num_seqs] (device, written) -- the slot of position
+ *                L - 1, or -1 when L == 0 (then nothing is stored); NULL to
+ *                not keep the slots
+ * Preconditions: the new tokens' slots are distinct, and no block holding a
+ * new token is shared with another table; with a shared prefix, every new
+ * token lies past it (L - 1 >= shared_prefix_blocks * block_size): a write
+ * into a shared block needs a copy-on-write first (the book's §6). A table
+ * entry outside [0, num_blocks) stores nothing.
+ * Workspace (pa_decode_cascade_workspace_size), partitioning, stream and
+ * errors: those of pa_decode_cascade, plus PA_ERR_NULL for a NULL k or v,
+ * PA_ERR_UNSUPPORTED for k / v not 16-byte aligned and PA_ERR_SHAPE for
+ * num_blocks * block_size above INT32_MAX (slots are int32).
+ */
+PA_API int pa_decode_append(const void* q, const void* k, const void* v, void* key_cache,
+                            void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, float scale, void* out,
+                            int32_t* slot_mapping, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                            int64_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, int32_t shared_prefix_blocks,
+                            int32_t partition_size, int32_t dtype, void* workspace,
+                            size_t workspace_size, void* stream);
+
+/*
+ * pa_decode_append_fp8 -- pa_decode_append over FP8 (E4M3) caches: the new
+ * rows are stored as pa_cache_write_fp8 stores them (k / v in dtype,
+ * quantized with k_scale / v_scale) and the step attends as pa_decode_fp8
+ * does, over the stored codes. No shared-prefix form. Workspace
+ * (pa_decode_workspace_size), errors and preconditions: those of
+ * pa_decode_fp8 and pa_decode_append.
+ */
+PA_API int pa_decode_append_fp8(const void* q, const void* k, const void* v, void* key_cache,
+                                void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, float k_scale,
+                                float v_scale, void* out, int32_t* slot_mapping,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size, int64_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int32_t partition_size, int32_t dtype, void* workspace,
+                                size_t workspace_size, void* stream);
+
+/*
  * Prefill batches ("01. PagedAttention 详解" §4, prefill phase: a prompt's N
  * tokens get their K/V written into the blocks the table points to, then
  * attention runs over them). Sequence s holds L = context_lens[s] positions

@@ -147,13 +147,39 @@ int check_cache_write(const void* k, const void* v, const void* key_cache,
 }
 
 // Shared body of pa_decode and pa_decode_fp8.
+// The new tokens a write-then-attend call stores before attending (all
+// nullptr for a plain decode).
+struct Append {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int32_t* slots = nullptr;
+};
+
+// Host checks of an append: both rows present and 16-byte aligned, slots
+// representable in int32.
+int check_append(const Append& ap, int64_t num_blocks, int32_t block_size) {
+  if (!ap.k && !ap.v) return PA_OK;
+  if (!ap.k || !ap.v) return PA_ERR_NULL;
+  if (!aligned16(ap.k) || !aligned16(ap.v)) return PA_ERR_UNSUPPORTED;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+void set_append(pa::DecodeParams& a, const Append& ap, float k_scale, float v_scale) {
+  a.k_new = (const uint16_t*)ap.k;
+  a.v_new = (const uint16_t*)ap.v;
+  a.slots_out = ap.k ? ap.slots : nullptr;
+  a.k_scale_w = k_scale;
+  a.v_scale_w = v_scale;
+}
+
 int decode_impl(const void* q, const void* key_cache, const void* value_cache, bool fp8_cache,
                 float k_scale, float v_scale, const int32_t* block_tables,
                 const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                 int32_t partition_size, int32_t dtype, void* workspace, size_t workspace_size,
-                void* stream) {
+                void* stream, const Append& ap = Append()) {
   if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
       num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
@@ -174,6 +200,8 @@ int decode_impl(const void* q, const void* key_cache, const void* value_cache, b
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
     return PA_ERR_UNSUPPORTED;
+  const int ast = check_append(ap, num_blocks, block_size);
+  if (ast != PA_OK) return ast;
 
   int cus = device_cu_count();
   if (cus <= 0) cus = kFallbackCUs;
@@ -228,6 +256,7 @@ int decode_impl(const void* q, const void* key_cache, const void* value_cache, b
     a.seq_major = 0;
     clear_sched(a);
   }
+  set_append(a, ap, k_scale, v_scale);
   const hipError_t e =
       pa::launch_decode(a, dtype, fp8_cache, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -254,6 +283,95 @@ CascadePlan cascade_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t block_s
   c.chunks = (int32_t)ceil_div(c.prefix_len, pa::kPrefixChunk);
   c.slots = c.chunks + c.num_parts;
   return c;
+}
+
+// Shared body of pa_decode_cascade and pa_decode_append.
+int cascade_impl(const void* q, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_size, int32_t block_size, int64_t num_blocks,
+                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                 int32_t shared_prefix_blocks, int32_t partition_size, int32_t dtype,
+                 void* workspace, size_t workspace_size, void* stream, const Append& ap) {
+  if (shared_prefix_blocks < 0 || shared_prefix_blocks > max_blocks_per_seq) return PA_ERR_SHAPE;
+  if (shared_prefix_blocks == 0)
+    return decode_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_tables, context_lens,
+                       scale, out, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
+                       workspace, workspace_size, stream, ap);
+  // Same validation as pa_decode (run with a single pass, which enqueues nothing
+  // when it fails and is not used when it passes).
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
+      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  // A shared prefix lives in the pool; the matrix-core kernel also relies on
+  // slot 0 existing (a masked position reads it).
+  if (num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+  const int ast = check_append(ap, num_blocks, block_size);
+  if (ast != PA_OK) return ast;
+
+  int cus = device_cu_count();
+  if (cus <= 0) cus = kFallbackCUs;
+  const CascadePlan c = cascade_plan(num_seqs, num_kv_heads, block_size, max_context_len,
+                                     shared_prefix_blocks, partition_size, cus);
+  const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, c.slots);
+  if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)num_seqs * group;
+
+  pa::DecodeParams a;
+  a.q = (const uint16_t*)q;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.bt = block_tables;
+  a.lens = context_lens;
+  a.out = (uint16_t*)out;
+  char* ws = (char*)workspace;
+  a.ws_m = (float*)(ws + lay.m_off);
+  a.ws_l = (float*)(ws + lay.l_off);
+  a.ws_o = (float*)(ws + lay.o_off);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.v_scale = 1.f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.log2_block_size = ilog2_exact(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.len_cap = max_context_len;
+  a.part_tokens = c.part_tokens;
+  a.num_parts = c.num_parts;
+  a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
+  a.tok_offset = c.prefix_len;
+  a.slot_base = c.chunks;
+  a.part_stride = c.slots;
+  a.always_combine = 0;     // one-partition suffixes fold the prefix in the partition kernel
+  a.prefix_len = c.prefix_len;
+  a.prefix_chunks = c.chunks;
+  const int rows_per_wg = pa::cascade_rows_per_wg(head_size);
+  a.prefix_row_tiles = (int32_t)((rows + rows_per_wg - 1) / rows_per_wg);
+  set_sched(a, workspace, cus, false, group);
+  set_append(a, ap, 1.f, 1.f);
+  const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -390,83 +508,50 @@ int pa_decode_cascade(const void* q, const void* key_cache, const void* value_ca
                       int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t shared_prefix_blocks, int32_t partition_size, int32_t dtype,
                       void* workspace, size_t workspace_size, void* stream) {
-  if (shared_prefix_blocks < 0 || shared_prefix_blocks > max_blocks_per_seq) return PA_ERR_SHAPE;
-  if (shared_prefix_blocks == 0)
-    return decode_impl(q, key_cache, value_cache, false, 1.f, 1.f, block_tables, context_lens,
-                       scale, out, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
-                       num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
-                       workspace, workspace_size, stream);
-  // Same validation as pa_decode (run with a single pass, which enqueues nothing
-  // when it fails and is not used when it passes).
-  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
-  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 || block_size < 1 ||
-      num_blocks < 0 || max_blocks_per_seq < 1 || max_context_len < 0)
-    return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
-  const int group = num_q_heads / num_kv_heads;
-  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
-  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
-    return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  // A shared prefix lives in the pool; the matrix-core kernel also relies on
-  // slot 0 existing (a masked position reads it).
-  if (num_blocks < 1) return PA_ERR_SHAPE;
-  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
-  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !out)
-    return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
-    return PA_ERR_UNSUPPORTED;
-
-  int cus = device_cu_count();
-  if (cus <= 0) cus = kFallbackCUs;
-  const CascadePlan c = cascade_plan(num_seqs, num_kv_heads, block_size, max_context_len,
-                                     shared_prefix_blocks, partition_size, cus);
-  const SplitLayout lay = split_layout(num_seqs, num_q_heads, head_size, c.slots);
-  if (!workspace || workspace_size < lay.total) return PA_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_UNSUPPORTED;
-  const int64_t rows = (int64_t)num_seqs * group;
-
-  pa::DecodeParams a;
-  a.q = (const uint16_t*)q;
-  a.kc = key_cache;
-  a.vc = value_cache;
-  a.bt = block_tables;
-  a.lens = context_lens;
-  a.out = (uint16_t*)out;
-  char* ws = (char*)workspace;
-  a.ws_m = (float*)(ws + lay.m_off);
-  a.ws_l = (float*)(ws + lay.l_off);
-  a.ws_o = (float*)(ws + lay.o_off);
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.v_scale = 1.f;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.block_size = block_size;
-  a.log2_block_size = ilog2_exact(block_size);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.len_cap = max_context_len;
-  a.part_tokens = c.part_tokens;
-  a.num_parts = c.num_parts;
-  a.seq_major = (int64_t)num_seqs * num_kv_heads < cus ? 1 : 0;
-  a.tok_offset = c.prefix_len;
-  a.slot_base = c.chunks;
-  a.part_stride = c.slots;
-  a.always_combine = 0;     // one-partition suffixes fold the prefix in the partition kernel
-  a.prefix_len = c.prefix_len;
-  a.prefix_chunks = c.chunks;
-  const int rows_per_wg = pa::cascade_rows_per_wg(head_size);
-  a.prefix_row_tiles = (int32_t)((rows + rows_per_wg - 1) / rows_per_wg);
-  set_sched(a, workspace, cus, false, group);
-  const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return cascade_impl(q, key_cache, value_cache, block_tables, context_lens, scale, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, shared_prefix_blocks, partition_size,
+                      dtype, workspace, workspace_size, stream, Append());
 }
+
+int pa_decode_append(const void* q, const void* k, const void* v, void* key_cache,
+                     void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+                     float scale, void* out, int32_t* slot_mapping, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                     int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int32_t shared_prefix_blocks,
+                     int32_t partition_size, int32_t dtype, void* workspace,
+                     size_t workspace_size, void* stream) {
+  if (num_seqs > 0 && (!k || !v)) return PA_ERR_NULL;
+  Append ap;
+  ap.k = k;
+  ap.v = v;
+  ap.slots = slot_mapping;
+  return cascade_impl(q, key_cache, value_cache, block_tables, context_lens, scale, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, shared_prefix_blocks, partition_size,
+                      dtype, workspace, workspace_size, stream, ap);
+}
+
+int pa_decode_append_fp8(const void* q, const void* k, const void* v, void* key_cache,
+                         void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, float k_scale, float v_scale,
+                         void* out, int32_t* slot_mapping, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                         void* workspace, size_t workspace_size, void* stream) {
+  if (num_seqs > 0 && (!k || !v)) return PA_ERR_NULL;
+  Append ap;
+  ap.k = k;
+  ap.v = v;
+  ap.slots = slot_mapping;
+  return decode_impl(q, key_cache, value_cache, true, k_scale, v_scale, block_tables,
+                     context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_size,
+                     block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
+                     dtype, workspace, workspace_size, stream, ap);
+}
+
 
 
 int pa_prefill_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -58,35 +58,6 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(
   }
 }
 
-// Eight 2-byte source values -> eight E4M3 codes (two words, lowest
-// dimension in the lowest byte): y = fp32(x) / scale (IEEE division),
-// clamped to +-448, rounded to nearest even by v_cvt_pk_fp8_f32; NaN -> 0x7F.
-template <class ST>
-__device__ __forceinline__ u32x2_t encode_fp8x8(uint4 x, float scale) {
-  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-  u32x2_t out;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    float y[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      y[2 * j] = Storage<ST>::lo(xw[2 * w + j]) / scale;
-      y[2 * j + 1] = Storage<ST>::hi(xw[2 * w + j]) / scale;
-    }
-    float c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(y[j], -448.f), 448.f);
-    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-    packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], packed, true);
-    uint32_t p = (uint32_t)packed;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (y[j] != y[j]) p = (p & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
-    out[w] = p;
-  }
-  return out;
-}
-
 // One thread per 8 elements of a token's [Hkv, D] row, for k and v alike.
 template <class ST>
 __global__ __launch_bounds__(kWriteThreads) void cache_write_fp8_kernel(

@@ -30,6 +30,8 @@
 //    becomes -inf and the V row is replaced by zeros, so whatever those slots
 //    hold (even NaN) cannot reach the result. Table entries past the last
 //    block are never read.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -57,6 +59,31 @@ __device__ __forceinline__ void fold_prefix(const DecodeParams& a, int64_t oh, i
   M = Mn;
 }
 
+// Write-then-attend: the new token of sequence s (position app = L - 1) is
+// stored at its slot table[app / bs] * bs + app % bs, kv head g's part by
+// the first LPR threads (one token row of lanes, DL dimensions each); the
+// slot is recorded once per sequence (kv head 0). A table entry outside the
+// pool stores nothing, as the separate cache write skips such slots.
+template <class KV, int DL, int LPR>
+__device__ __forceinline__ void append_row(const DecodeParams& a, int s, int g, int app, int D,
+                                           int tid) {
+  if (app < 0) {
+    if (g == 0 && tid == 0 && a.slots_out) a.slots_out[s] = -1;
+    return;
+  }
+  const int32_t blk = a.bt[(int64_t)s * a.max_blocks_per_seq + (app >> a.log2_block_size)];
+  const int32_t slot = blk * a.block_size + (app & (a.block_size - 1));
+  if (g == 0 && tid == 0 && a.slots_out) a.slots_out[s] = slot;
+  if (tid >= LPR || (uint64_t)(uint32_t)blk >= (uint64_t)a.num_blocks) return;
+  const int64_t src = ((int64_t)s * a.num_kv_heads + g) * D + tid * DL;
+  const int64_t dst = (int64_t)slot * a.num_kv_heads * D + (int64_t)g * D + tid * DL;
+  using elem = typename KV::elem;
+  KV::store(const_cast<elem*>(static_cast<const elem*>(a.kc)) + dst,
+            KV::from_src(a.k_new + src, a.k_scale_w));
+  KV::store(const_cast<elem*>(static_cast<const elem*>(a.vc)) + dst,
+            KV::from_src(a.v_new + src, a.v_scale_w));
+}
+
 constexpr float kEmptyMax = -1.0e30f;  // running max before any token: finite, so
                                        // exp2(m_old - m_new) never sees inf - inf
 constexpr float kSlack = 8.f;              // lazy softmax reference: weights stay <= 2^8
@@ -76,7 +103,9 @@ struct DecodeLds {
 
 // One work item: kv head g, sequence s, partition p. Uniform over the
 // work-group (every thread takes the same path and the same barriers).
-template <class DT, class KT, int D, int G>
+// APP: the call appends each sequence's new token (write-then-attend);
+// instantiated separately so that a plain decode carries none of its code.
+template <class DT, class KT, int D, int G, bool APP>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
                                             DecodeLds<D, G>& sm) {
   using S = Storage<DT>;
@@ -100,7 +129,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int start = a.tok_offset + p * a.part_tokens;
   const int tid = threadIdx.x;
+  // Position of the appended token, or -1 (nothing appended, or L = 0).
+  const int app = APP ? L - 1 : -1;
   if (start >= L) {
+    // The first partition of a sequence with no token past the offset stores
+    // its appended token (inside a cascade's shared prefix, which callers
+    // must not do: the prefix kernel has already read that block).
+    if (APP && p == 0) append_row<KV, DL, LPR>(a, s, g, app, D, tid);
     if (p == 0 && !a.always_combine) {
       // No token past the offset: an empty sequence stays zero; in a cascade a
       // sequence that ends inside the shared prefix is the prefix partials alone.
@@ -118,6 +153,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
     return;
   }
   const int end = min(L, start + a.part_tokens);
+  // With an append, the partition holding position L - 1 reads its cached
+  // positions [start, L - 1) from the caches and takes the new token from
+  // k_new / v_new (after its tiles, below): the slot it stores is never read
+  // in this launch, so no ordering between the store and the loads is needed.
+  const bool own_app = APP && app >= start && app < end;
+  const int end_main = own_app ? app : end;
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -156,8 +197,100 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   const int bs = a.block_size;
   const int lbs = a.log2_block_size;
   const int first_blk = start >> lbs;            // start is block aligned
-  const int end_blk = ((end - 1) >> lbs) + 1;    // one past the last block read
+  // one past the last block read (first_blk when only the new token is left)
+  const int end_blk = end_main > start ? ((end_main - 1) >> lbs) + 1 : first_blk;
   const float sl2 = a.scale_log2;
+
+  // Online-softmax update of every token row with one 16-token tile whose K/V
+  // rows are in kr / vr; positions >= tend are masked out.
+  auto attend = [&](const int ts, const int tend, row_t (&kr)[TG], row_t (&vr)[TG]) {
+    float lg[G][TG];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) lg[h][tg] = row_sum<LPR>(KV::dot(qw[h], kr[tg], 0.f)) * sl2;
+
+    if (ts + kTile > tend) {                   // tail tile: mask positions >= tend
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        const bool ok = ts + tg * ROWS + row < tend;
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[h][tg] = ok ? lg[h][tg] : -INFINITY;
+        vr[tg] = ok ? vr[tg] : KV::zero();
+      }
+    }
+    uint32_t vw[TG][DL / 2];                   // V rows as packed QT pairs
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) KV::pairs(vr[tg], vw[tg]);
+
+    // Online softmax with a lazily moved reference: a row's m only moves
+    // when the tile's max exceeds it by more than kSlack (log2 units), so
+    // the weights 2^(s - m) stay below 2^kSlack and the accumulators are
+    // rescaled only on such tiles -- skipped by the whole wave when no row
+    // moved. sum 2^(s-m) v / sum 2^(s-m) does not depend on m.
+    float pr[G][TG], alpha[G];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = lg[h][0];
+#pragma unroll
+      for (int tg = 1; tg < TG; ++tg) mx = fmaxf(mx, lg[h][tg]);
+      const bool up = mx > m[h] + kSlack;
+      const float mn = up ? mx : m[h];
+      alpha[h] = up ? fast_exp2(m[h] - mn) : 1.f;
+      moved |= up;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) pr[h][tg] = fast_exp2(lg[h][tg] - mn);
+      m[h] = mn;
+    }
+    if (__ballot(moved) != 0) {                  // uniform
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] *= alpha[h];
+#pragma unroll
+        for (int d = 0; d < DL; ++d) acc[h][d] *= alpha[h];
+      }
+    }
+    // p.V on v_dot2 over token pairs: the lane's rows tg and tg+1 hold the
+    // same DL dimensions of two tokens, so (v_A,d, v_B,d) is one packed word
+    // and (p_A, p_B) -- the weights rounded to QT -- another; the exp-sum
+    // takes the same rounded weights (a dot2 with (1, 1)).
+#pragma unroll
+    for (int i = 0; i < TG / 2; ++i) {
+      uint32_t vlo[DL / 2], vhi[DL / 2];         // dimension 2e / 2e+1 of tokens A, B
+#pragma unroll
+      for (int e = 0; e < DL / 2; ++e) {
+        vlo[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x05040100u);
+        vhi[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x07060302u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pp = S::pack2(pr[h][2 * i], pr[h][2 * i + 1]);
+        l[h] = S::dot2(pp, S::kOnes, l[h]);
+#pragma unroll
+        for (int e = 0; e < DL / 2; ++e) {
+          acc[h][2 * e] = S::dot2(pp, vlo[e], acc[h][2 * e]);
+          acc[h][2 * e + 1] = S::dot2(pp, vhi[e], acc[h][2 * e + 1]);
+        }
+      }
+    }
+  };
+
+  // The new token goes to the wave that would take the next tile (tiles are
+  // dealt round-robin from wave 0; a table chunk holds a multiple of NW
+  // tiles), so it evens out the waves' work instead of adding to it. With a
+  // 2-byte cache that wave loads the new rows before its tiles, so their
+  // latency hides behind the loop (an FP8 row would hold twice the registers
+  // before quantization and is loaded after the loop).
+  const int app_wave = ((end_main - start + kTile - 1) / kTile) % NW;
+  const bool app_here = own_app && wave == app_wave;   // uniform
+  const int64_t app_src = ((int64_t)s * Hkv + g) * D + col * DL;
+  constexpr bool kEarlyRows = !std::is_same<KT, Fp8>::value;
+  row_t kn_early{}, vn_early{};
+  if (kEarlyRows && app_here) {
+    kn_early = KV::from_src(a.k_new + app_src, a.k_scale_w);
+    vn_early = KV::from_src(a.v_new + app_src, a.v_scale_w);
+  }
 
   for (int cb = first_blk; cb < end_blk; cb += kTableChunk) {
     const int nb = min(kTableChunk, end_blk - cb);
@@ -165,7 +298,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
     for (int i = tid; i < nb; i += NT) s_tbl[i] = bt_row[cb + i];
     __syncthreads();
     const int t0 = cb << lbs;
-    const int t1 = min(end, (cb + nb) << lbs);
+    const int t1 = min(end_main, (cb + nb) << lbs);
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
     for (int it = wave; it < ntiles; it += NW) {
@@ -181,76 +314,32 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) vr[tg] = KV::load(vc + base + tg * ROWS * tok_stride);
 
-      float lg[G][TG];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int tg = 0; tg < TG; ++tg) lg[h][tg] = row_sum<LPR>(KV::dot(qw[h], kr[tg], 0.f)) * sl2;
-
-      if (ts + kTile > end) {                    // tail tile: mask positions >= end
-#pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-          const bool ok = ts + tg * ROWS + row < end;
-#pragma unroll
-          for (int h = 0; h < G; ++h) lg[h][tg] = ok ? lg[h][tg] : -INFINITY;
-          vr[tg] = ok ? vr[tg] : KV::zero();
-        }
+      attend(ts, end_main, kr, vr);
+    }
+  }
+  if (app_here) {
+    // The new token, as a tile whose rows all hold it and whose positions
+    // past app are masked: token row 0 takes it into its softmax state, and
+    // the row-0 lanes store it at the slot, as the separate cache write does;
+    // a table entry outside the pool drops both, as a skipped tile does.
+    const int32_t blk = __builtin_amdgcn_readfirstlane(bt_row[app >> lbs]);
+    const int32_t slot = blk * bs + (app & (bs - 1));
+    if (g == 0 && lane == 0 && a.slots_out) a.slots_out[s] = slot;
+    if ((uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks) {
+      const row_t kn = kEarlyRows ? kn_early : KV::from_src(a.k_new + app_src, a.k_scale_w);
+      const row_t vn = kEarlyRows ? vn_early : KV::from_src(a.v_new + app_src, a.v_scale_w);
+      if (row == 0) {
+        const int64_t dst = (int64_t)slot * tok_stride + (int64_t)g * D + col * DL;
+        KV::store(const_cast<elem*>(kc) + dst, kn);
+        KV::store(const_cast<elem*>(vc) + dst, vn);
       }
-      uint32_t vw[TG][DL / 2];                   // V rows as packed QT pairs
+      row_t kr[TG], vr[TG];
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) KV::pairs(vr[tg], vw[tg]);
-
-      // Online softmax with a lazily moved reference: a row's m only moves
-      // when the tile's max exceeds it by more than kSlack (log2 units), so
-      // the weights 2^(s - m) stay below 2^kSlack and the accumulators are
-      // rescaled only on such tiles -- skipped by the whole wave when no row
-      // moved. sum 2^(s-m) v / sum 2^(s-m) does not depend on m.
-      float pr[G][TG], alpha[G];
-      bool moved = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = lg[h][0];
-#pragma unroll
-        for (int tg = 1; tg < TG; ++tg) mx = fmaxf(mx, lg[h][tg]);
-        const bool up = mx > m[h] + kSlack;
-        const float mn = up ? mx : m[h];
-        alpha[h] = up ? fast_exp2(m[h] - mn) : 1.f;
-        moved |= up;
-#pragma unroll
-        for (int tg = 0; tg < TG; ++tg) pr[h][tg] = fast_exp2(lg[h][tg] - mn);
-        m[h] = mn;
+      for (int tg = 0; tg < TG; ++tg) {
+        kr[tg] = kn;
+        vr[tg] = vn;
       }
-      if (__ballot(moved) != 0) {                  // uniform
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          l[h] *= alpha[h];
-#pragma unroll
-          for (int d = 0; d < DL; ++d) acc[h][d] *= alpha[h];
-        }
-      }
-      // p.V on v_dot2 over token pairs: the lane's rows tg and tg+1 hold the
-      // same DL dimensions of two tokens, so (v_A,d, v_B,d) is one packed word
-      // and (p_A, p_B) -- the weights rounded to QT -- another; the exp-sum
-      // takes the same rounded weights (a dot2 with (1, 1)).
-#pragma unroll
-      for (int i = 0; i < TG / 2; ++i) {
-        uint32_t vlo[DL / 2], vhi[DL / 2];         // dimension 2e / 2e+1 of tokens A, B
-#pragma unroll
-        for (int e = 0; e < DL / 2; ++e) {
-          vlo[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x05040100u);
-          vhi[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x07060302u);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint32_t pp = S::pack2(pr[h][2 * i], pr[h][2 * i + 1]);
-          l[h] = S::dot2(pp, S::kOnes, l[h]);
-#pragma unroll
-          for (int e = 0; e < DL / 2; ++e) {
-            acc[h][2 * e] = S::dot2(pp, vlo[e], acc[h][2 * e]);
-            acc[h][2 * e + 1] = S::dot2(pp, vhi[e], acc[h][2 * e + 1]);
-          }
-        }
-      }
+      attend(app, app + 1, kr, vr);
     }
   }
 
@@ -361,7 +450,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 // the grid. With few pairs (long contexts) the sequence index comes last, so
 // one sequence's partitions run together; each order measured faster in its
 // regime.
-template <class DT, class KT, int D, int G>
+template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
   int wg = blockIdx.x;
@@ -369,7 +458,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   wg /= a.num_kv_heads;
   const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
   const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
-  decode_item<DT, KT, D, G>(a, g, s, p, sm);
+  decode_item<DT, KT, D, G, APP>(a, g, s, p, sm);
 }
 
 // Persistent grid: gridDim.x (at most the item count) work-groups walk the
@@ -384,7 +473,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
 // schedule. One counter serves the whole chip: splitting it per XCD (each
 // XCD's work-groups on their own share of the items, with or without
 // stealing at the end) measured 3-9% slower.
-template <class DT, class KT, int D, int G>
+template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
   __shared__ int s_item[2];
@@ -398,7 +487,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int g = it % Hkv;
     const int s = (it / Hkv) % a.num_seqs;
     const int p = it / (Hkv * a.num_seqs);
-    decode_item<DT, KT, D, G>(a, g, s, p, sm);
+    decode_item<DT, KT, D, G, APP>(a, g, s, p, sm);
     if (!counted) {
       item += grid;
       continue;
@@ -571,20 +660,20 @@ hipError_t launch_combine(const DecodeParams& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class DT, class KT, int D, int G>
-hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
+template <class DT, class KT, int D, int G, bool APP>
+hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   const uint64_t nwg = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
   const bool combine = a.num_parts > 1 || a.always_combine;
   if (a.sched != nullptr && combine && a.persist_grid > 0) {
     const uint32_t grid = (uint32_t)(nwg < (uint64_t)a.persist_grid ? nwg : a.persist_grid);
-    hipLaunchKernelGGL((decode_persistent_kernel<DT, KT, D, G>), dim3(grid),
+    hipLaunchKernelGGL((decode_persistent_kernel<DT, KT, D, G, APP>), dim3(grid),
                        dim3(kDecodeWaves * 64), 0, st, a);
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
-    hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G>), dim3((uint32_t)nwg),
+    hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP>), dim3((uint32_t)nwg),
                        dim3(kDecodeWaves * 64), 0, st, b);
     if (!combine) return hipGetLastError();
     const hipError_t e = hipGetLastError();
@@ -594,6 +683,12 @@ hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine<DT, D>(a, st);
+}
+
+template <class DT, class KT, int D, int G>
+hipError_t launch_dg(const DecodeParams& a, hipStream_t st) {
+  return a.k_new != nullptr ? launch_dga<DT, KT, D, G, true>(a, st)
+                            : launch_dga<DT, KT, D, G, false>(a, st);
 }
 
 template <class DT, class KT, int D>

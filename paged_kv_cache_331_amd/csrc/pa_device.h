@@ -127,6 +127,35 @@ __device__ __forceinline__ u32x2_t load_stream8(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
 
+// Eight 2-byte source values -> eight E4M3 codes (two words, lowest
+// dimension in the lowest byte): y = fp32(x) / scale (IEEE division),
+// clamped to +-448, rounded to nearest even by v_cvt_pk_fp8_f32; NaN -> 0x7F.
+template <class ST>
+__device__ __forceinline__ u32x2_t encode_fp8x8(uint4 x, float scale) {
+  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  u32x2_t out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      y[2 * j] = Storage<ST>::lo(xw[2 * w + j]) / scale;
+      y[2 * j + 1] = Storage<ST>::hi(xw[2 * w + j]) / scale;
+    }
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], packed, true);
+    uint32_t p = (uint32_t)packed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (y[j] != y[j]) p = (p & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
+    out[w] = p;
+  }
+  return out;
+}
+
 // The slice of one cached K or V row a lane holds: DL consecutive dimensions.
 // QT is the query's type (fp16 / bf16), KT the cache element type.
 template <class QT, class KT, int DL> struct Kv;
@@ -154,6 +183,14 @@ template <class QT> struct Kv<QT, QT, 8> {
     for (int e = 0; e < 4; ++e) w[e] = v[e];
   }
   static __device__ __forceinline__ row zero() { return row{0u, 0u, 0u, 0u}; }
+  // The lane's slice of a new token's row in the query's type (src points at
+  // its first dimension), as the cache stores it: a copy (scale unused).
+  static __device__ __forceinline__ row from_src(const uint16_t* src, float) {
+    return *reinterpret_cast<const u32x4_t*>(src);
+  }
+  static __device__ __forceinline__ void store(elem* dst, row r) {
+    *reinterpret_cast<u32x4_t*>(dst) = r;
+  }
 };
 
 // Two E4M3 codes (the low or high 16 bits of w, lower address first) as a
@@ -198,6 +235,21 @@ template <class QT, int DL> struct Kv<QT, Fp8, DL> {
     }
   }
   static __device__ __forceinline__ row zero() { return row{}; }
+  // The lane's DL dimensions of a new token's row quantized as the FP8 cache
+  // write does: e4m3(fp32(x) / scale).
+  static __device__ __forceinline__ row from_src(const uint16_t* src, float scale) {
+    row r;
+#pragma unroll
+    for (int c = 0; c < DL / 8; ++c) {
+      const u32x2_t w = encode_fp8x8<QT>(*reinterpret_cast<const uint4*>(src + 8 * c), scale);
+      r[2 * c] = w[0];
+      r[2 * c + 1] = w[1];
+    }
+    return r;
+  }
+  static __device__ __forceinline__ void store(elem* dst, row r) {
+    *reinterpret_cast<row*>(dst) = r;
+  }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -53,6 +53,15 @@ struct DecodeParams {
   unsigned long long* sched;  // nullptr: one work-group per item
   uint32_t sched_tag;
   int32_t persist_grid;       // 0: one work-group per item
+  // Write-then-attend in the same launch: each sequence's new token (position
+  // L-1) is stored into the caches at its slot and used as that position's
+  // K/V row. The work item whose partition holds position L-1 stores the
+  // row of its kv head; the one of kv head 0 also records the slot.
+  const uint16_t* k_new = nullptr;  // [B, Hkv, D] in q's type; nullptr: nothing appended
+  const uint16_t* v_new = nullptr;  // [B, Hkv, D]
+  int32_t* slots_out = nullptr;     // [B]: slot of position L-1, -1 if L = 0 (nullptr: not kept)
+  float k_scale_w = 1.f;            // FP8 cache: the write stores e4m3(fp32(x) / scale)
+  float v_scale_w = 1.f;
 };
 
 // Bytes reserved for the scheduler word at the head of a split-K workspace,

@@ -59,6 +59,12 @@ SIGNATURES = {
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz,
                                      _vp]),
+    "pa_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32,
+                                        _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
+                                        _i32, _vp, _sz, _vp]),
+    "pa_decode_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32,
+                                            _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
+                                            _i32, _i32, _i32, _vp, _sz, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -266,6 +272,72 @@ def decode_cascade(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.
                                   int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
                                   _stream(stream))
     _check("pa_decode_cascade", st)
+    return out
+
+
+def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_cache: torch.Tensor,
+                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, max_context_len: int,
+                  shared_prefix_blocks: int = 0, out: Optional[torch.Tensor] = None,
+                  slot_mapping: Optional[torch.Tensor] = None, partition_size: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Whole decode step in one call: store each sequence's new k/v ([B, Hkv, D]) at the
+    slot of position L-1 (written to ``slot_mapping`` if given), then attend."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_cascade_workspace_size(B, Hq, D, bs, max_context_len, shared_prefix_blocks,
+                                         partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    slots_ptr = _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None
+    st = load().pa_decode_append(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                 _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                                 _dev(block_tables, "block_tables"),
+                                 _dev(context_lens, "context_lens"), float(scale),
+                                 _dev(out, "out"), slots_ptr, B, Hq, Hkv, D, bs, NB, MB,
+                                 int(max_context_len), int(shared_prefix_blocks),
+                                 int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
+                                 _stream(stream))
+    _check("pa_decode_append", st)
+    return out
+
+
+def decode_append_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      k_scale: float, v_scale: float, max_context_len: int,
+                      out: Optional[torch.Tensor] = None,
+                      slot_mapping: Optional[torch.Tensor] = None, partition_size: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_append over uint8 E4M3 caches: the new rows are quantized with the scales."""
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise TypeError("FP8 caches are uint8 tensors of E4M3 codes")
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(B, Hq, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    slots_ptr = _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None
+    st = load().pa_decode_append_fp8(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                     _dev(key_cache, "key_cache"),
+                                     _dev(value_cache, "value_cache"),
+                                     _dev(block_tables, "block_tables"),
+                                     _dev(context_lens, "context_lens"), float(scale),
+                                     float(k_scale), float(v_scale), _dev(out, "out"), slots_ptr,
+                                     B, Hq, Hkv, D, bs, NB, MB, int(max_context_len),
+                                     int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
+                                     _stream(stream))
+    _check("pa_decode_append_fp8", st)
     return out
 
 

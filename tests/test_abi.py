@@ -34,7 +34,8 @@ def test_header_declares_expected_api():
                                   "pa_prefill_slot_mapping", "pa_pool_create",
                                   "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count",
                                   "pa_pool_allocate", "pa_pool_free", "pa_pool_share",
-                                  "pa_pool_copy_on_write", "pa_copy_blocks"])
+                                  "pa_pool_copy_on_write", "pa_copy_blocks",
+                                  "pa_decode_append", "pa_decode_append_fp8"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
@@ -297,3 +298,46 @@ def test_copy_blocks_validation(lib, kw, code):
     st = pa.load().pa_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["NB"], a["bs"],
                                   a["Hkv"], a["D"], a["eb"], a["stream"])
     assert st == code
+
+
+def _append(fp8=False, **kw):
+    a = dict(q=16, k=16, v=16, kc=16, vc=16, bt=16, lens=16, scale=0.125, ks=1.0, vs=1.0, out=16,
+             slots=16, B=2, Hq=4, Hkv=4, D=128, bs=16, NB=10, MB=4, maxlen=64, spb=0, P=-1,
+             dtype=F, ws=None, wss=0, stream=None)
+    a.update(kw)
+    lib = pa.load()
+    if fp8:
+        return lib.pa_decode_append_fp8(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"],
+                                        a["lens"], a["scale"], a["ks"], a["vs"], a["out"],
+                                        a["slots"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                        a["NB"], a["MB"], a["maxlen"], a["P"], a["dtype"],
+                                        a["ws"], a["wss"], a["stream"])
+    return lib.pa_decode_append(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"], a["lens"],
+                                a["scale"], a["out"], a["slots"], a["B"], a["Hq"], a["Hkv"],
+                                a["D"], a["bs"], a["NB"], a["MB"], a["maxlen"], a["spb"], a["P"],
+                                a["dtype"], a["ws"], a["wss"], a["stream"])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1),
+    (dict(v=None), -1),
+    (dict(k=8), -4),                    # misaligned new row
+    (dict(v=24), -4),
+    (dict(NB=2**27, bs=32, MB=4, maxlen=64), -2),   # slots beyond int32
+    (dict(dtype=5), -3),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(D=96), -4),
+    (dict(q=None), -1),
+    (dict(P=16, ws=None, wss=0), -5),
+])
+def test_decode_append_validation(lib, fp8, kw, code):
+    assert _append(fp8, **kw) == code
+
+
+def test_decode_append_specific_errors(lib):
+    assert _append(spb=-1) == -2               # shared prefix out of range
+    assert _append(spb=5) == -2                # more blocks than a table holds
+    assert _append(True, ks=0.0) == -2         # FP8 scales must be finite and positive
+    assert _append(B=0, q=None, k=None, v=None, out=None) == 0
+    assert _append(True, B=0, q=None, k=None, v=None, out=None) == 0

@@ -1,0 +1,205 @@
+"""GPU parity of the one-call decode step (pa_decode_append, pa_decode_append_fp8):
+slot of each sequence's new token, its k/v stored into the caches, attention.
+
+Each case is checked two ways:
+  * against the fp64 CPU oracle: slots and the whole pools bit-exact
+    (oracle.slot_mapping / oracle.cache_write[_fp8]), attention within the
+    decode tolerance (2e-3 fp16, 1e-2 bf16);
+  * against the three separate calls on a second copy of the same inputs
+    (slot mapping, cache write, decode): identical slots and pools, outputs
+    within the same tolerance of each other (the one-call step adds the new
+    token's term in another order, so the last bits may differ).
+The slot the write fills holds NaN beforehand (and so do the tail slots past
+it), so an attention step that read the old row there would fail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_331_amd import pa, workloads as wl
+
+from _paged import (TOL, Device, down16, down8, max_err, oracle_caches, oracle_decode,
+                    poison_tails, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    pa.load()
+    assert torch.cuda.is_available()
+
+
+def _poison_write_slots(b: wl.Batch) -> None:
+    """NaN into the slot of position L-1 of every sequence (the write fills it)."""
+    nb = wl.nan_bits(b.cache_dtype)
+    bs = b.spec.block_size
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        if L > 0:
+            slot = oracle.physical_slot(b.block_tables[s], L - 1, bs)
+            b.key_cache[slot // bs, slot % bs] = nb
+            b.value_cache[slot // bs, slot % bs] = nb
+
+
+def _down(b, t):
+    return down8(t) if b.cache_dtype == "fp8" else down16(t)
+
+
+def _fused(b, d, P, ws=None, prefix_blocks=0):
+    slots = torch.full((b.num_seqs,), 12345, dtype=torch.int32, device="cuda")
+    if b.cache_dtype == "fp8":
+        out = pa.decode_append_fp8(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens,
+                                   float(b.scale), float(b.k_scale), float(b.v_scale),
+                                   b.max_context_len, slot_mapping=slots, partition_size=P,
+                                   workspace=ws)
+    else:
+        out = pa.decode_append(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens, float(b.scale),
+                               b.max_context_len, prefix_blocks, slot_mapping=slots,
+                               partition_size=P, workspace=ws)
+    torch.cuda.synchronize()
+    return slots, out
+
+
+def _separate(b, d, P, prefix_blocks=0):
+    slots = pa.decode_slot_mapping(d.bt, d.lens, b.spec.block_size)
+    if b.cache_dtype == "fp8":
+        pa.cache_write_fp8(d.k_new, d.v_new, d.kc, d.vc, slots, float(b.k_scale),
+                           float(b.v_scale))
+        out = pa.decode_fp8(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), float(b.k_scale),
+                            float(b.v_scale), b.max_context_len, partition_size=P)
+    else:
+        pa.cache_write(d.k_new, d.v_new, d.kc, d.vc, slots)
+        if prefix_blocks:
+            out = pa.decode_cascade(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale),
+                                    b.max_context_len, prefix_blocks, partition_size=P)
+        else:
+            out = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len,
+                            partition_size=P)
+    torch.cuda.synchronize()
+    return slots, out
+
+
+def _check(b, P, prefix_blocks=0, oracle_out=True):
+    _poison_write_slots(b)
+    poison_tails(b, True)
+    d1, d2 = Device(b), Device(b)
+    slots, out = _fused(b, d1, P, prefix_blocks=prefix_blocks)
+    slots2, out2 = _separate(b, d2, P, prefix_blocks)
+    kc, vc, ref_slots = oracle_caches(b, True)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots), "slots vs oracle"
+    assert np.array_equal(_down(b, d1.kc), kc), "key cache vs oracle"
+    assert np.array_equal(_down(b, d1.vc), vc), "value cache vs oracle"
+    assert torch.equal(slots, slots2)
+    assert torch.equal(d1.kc.view(torch.uint8), d2.kc.view(torch.uint8))
+    assert torch.equal(d1.vc.view(torch.uint8), d2.vc.view(torch.uint8))
+    assert bool(torch.isfinite(out.float()).all())
+    gap = float((out.float() - out2.float()).abs().max()) if out.numel() else 0.0
+    say(f"  fused vs separate max abs diff {gap:.3e}")
+    assert gap <= TOL[b.dtype], "fused vs separate"
+    if oracle_out:
+        ref = oracle_decode(b, kc, vc)
+        err = max_err(out, ref)
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[b.dtype]
+
+
+CASES = [("tiny_write", None, 0), ("tiny_write", None, -1), ("tiny_write", None, 32),
+         ("llama2_7b_mha", 6, 0), ("llama2_7b_mha", 6, 256), ("llama2_7b_mha", 8, 1024),
+         ("gqa_8b", 12, 0), ("gqa_8b", 12, 512), ("long_context_splitk", 1, 0),
+         ("llama2_7b_mha_fp8", 6, 0), ("llama2_7b_mha_fp8", 6, 256), ("gqa_8b_fp8", 12, 0),
+         ("gqa_8b_fp8", 12, 512)]
+
+
+@pytest.mark.parametrize("name,seqs,P", CASES)
+def test_append_small_all_outputs(name, seqs, P):
+    spec = wl.CONFIGS[name] if seqs is None else wl.small_variant(name, seqs)
+    b = wl.make_batch(spec)
+    say(f"append {name} B={b.num_seqs} P={P}")
+    _check(b, P)
+
+
+@pytest.mark.parametrize("P", [0, -1, 64])
+def test_append_cascade_small_all_outputs(P):
+    spec = wl.small_variant("prefix_shared_write", 6)
+    b = wl.make_batch(spec)
+    say(f"append cascade B={b.num_seqs} P={P}")
+    _check(b, P, prefix_blocks=spec.shared_prefix_blocks)
+
+
+@pytest.mark.parametrize("P", [0, 16])
+@pytest.mark.parametrize("cache", ["fp16", "fp8"])
+def test_append_edge_lengths(cache, P):
+    """L = 0 (slot -1, nothing stored, zero output), L = 1 (the new token alone:
+    out = v_new exactly for a 2-byte cache), and lengths at block edges; with
+    16-token partitions, L = 17 and 33 leave the new token alone in its
+    partition."""
+    spec = wl.CONFIGS["tiny_write"]
+    if cache == "fp8":
+        spec = wl.replace(spec, cache_dtype="fp8")
+    lens = [0, 1, 15, 16, 17, 32, 33, 100]
+    b = wl.make_batch(spec, lengths=lens)
+    say(f"append edge lengths cache={cache} P={P}")
+    _check(b, P)
+    d = Device(b)
+    slots, out = _fused(b, d, P)
+    assert int(slots[0]) == -1
+    assert not torch.any(out[0].float() != 0)
+    if cache == "fp16":
+        v1 = torch.from_numpy(b.v_new[1].view(np.int16)).cuda()
+        heads = spec.num_q_heads // spec.num_kv_heads
+        assert torch.equal(out[1].view(torch.int16),
+                           v1.repeat_interleave(heads, dim=0))
+
+
+def test_append_without_slot_output_and_workspace_reuse():
+    """slot_mapping may be NULL; two calls on one workspace (the second takes
+    the persistent grid's counter left by the first) give the same output bits
+    and pools, and stay within the tolerance of the separate calls."""
+    spec = wl.small_variant("llama2_7b_mha", 8)
+    b = wl.make_batch(spec)
+    _poison_write_slots(b)
+    d1, d2 = Device(b), Device(b)
+    ws = torch.empty(pa.decode_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size,
+                                              b.max_context_len, 1024),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for it in range(2):
+        say(f"append workspace reuse call {it}")
+        out = pa.decode_append(d1.q, d1.k_new, d1.v_new, d1.kc, d1.vc, d1.bt, d1.lens,
+                               float(b.scale), b.max_context_len, partition_size=1024,
+                               workspace=ws)
+        _, out2 = _separate(b, d2, 1024)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+        assert float((out.float() - out2.float()).abs().max()) <= TOL[b.dtype]
+        assert torch.equal(d1.kc.view(torch.int16), d2.kc.view(torch.int16))
+        assert torch.equal(d1.vc.view(torch.int16), d2.vc.view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_mha", "gqa_8b", "prefix_shared_write",
+                                  "llama2_7b_mha_fp8"])
+def test_append_full_size_matches_separate_calls(name):
+    """At full size, in the launch configuration the benchmark times: slots and
+    pools against the oracle, every output row against the separate calls
+    (whose own oracle parity the decode tests cover), and a sample of output
+    rows against the oracle."""
+    spec = wl.CONFIGS[name]
+    b = wl.make_batch(spec)
+    pb = spec.shared_prefix_blocks
+    say(f"append full {name} B={b.num_seqs}")
+    _check(b, 0, prefix_blocks=pb, oracle_out=False)
+    d = Device(b)
+    _, out = _fused(b, d, 0, prefix_blocks=pb)
+    kc, vc, _ = oracle_caches(b, True)
+    rng = np.random.default_rng(7)
+    seqs = sorted(rng.choice(b.num_seqs, size=4, replace=False).tolist())
+    ref = oracle.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype,
+                        seqs=seqs, cache_dtype=b.cache_dtype, k_scale=b.k_scale,
+                        v_scale=b.v_scale)
+    got = out[seqs].float().cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  sampled max abs err {err:.3e}")
+    assert err <= TOL[b.dtype]

@@ -523,7 +523,7 @@ def main(argv=None) -> int:
             "max_context_len": maxlen, "partition_size": args.partition_size,
             "partition_tokens_used": (args.partition_size if args.partition_size != 0 else
                                       pa.decode_partition_size(batch.num_seqs, spec.num_kv_heads,
-                                                               maxlen)),
+                                                               maxlen, 1 if fp8 else 2)),
             "step": ("one call (pa_decode_append" + ("_fp8" if fp8 else "") + "): slot mapping + "
                      "cache write + " if fused else "slot mapping + cache write + ") +
                     ("cascade decode (shared prefix)" if cascade else "decode"),

@@ -164,17 +164,21 @@ PA_API size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, in
  *
  * Returns the tokens per partition of the automatic choice, or -1 for a
  * single pass, for a batch of num_seqs sequences with num_kv_heads kv heads
- * whose longest context is max_context_len. The rule: the largest power of
- * two in [256, 4096] that still gives about four work-groups per compute
- * unit; at most 1024 when the (sequence, kv head) pairs alone give that many;
- * no split when the longest context is at most 1.5 partitions. num_cus <= 0
- * asks the current HIP device for its compute-unit count (256 if it cannot
- * be queried). Pure host arithmetic otherwise; no device work is enqueued.
- * Returns 0 for invalid sizes (num_seqs < 0, num_kv_heads < 1,
- * max_context_len < 0).
+ * whose longest context is max_context_len, over caches of cache_elem_bytes
+ * bytes per element (2: pa_decode and the cascade; 1: pa_decode_fp8). The
+ * rule: the largest power of two in [256, 4096] that still gives about four
+ * work-groups per compute unit; when the (sequence, kv head) pairs alone
+ * give that many, at most 1024 -- or 2048 for 2-byte elements when the
+ * longest context exceeds 3072 tokens; no split when the longest context is
+ * at most 1.5 partitions. num_cus <= 0 asks the current HIP device for its
+ * compute-unit count (256 if it cannot be queried). Pure host arithmetic
+ * otherwise; no device work is enqueued. Returns 0 for invalid sizes
+ * (num_seqs < 0, num_kv_heads < 1, max_context_len < 0, cache_elem_bytes not
+ * 1 or 2).
  */
 PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                        int32_t max_context_len, int32_t num_cus);
+                                        int32_t max_context_len, int32_t cache_elem_bytes,
+                                        int32_t num_cus);
 
 /*
  * pa_decode -- one decode step of paged attention.

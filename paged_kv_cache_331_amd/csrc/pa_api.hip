@@ -14,6 +14,7 @@ namespace {
 constexpr int kAutoMinPartition = 256;       // partition sizes an automatic choice may use
 constexpr int kAutoMaxPartition = 4096;
 constexpr int kAutoBalancedPartition = 1024;  // cap when the batch alone fills the chip
+constexpr int kAutoBalancedPartitionWide = 2048;  // the same cap for 2-byte rows and long tails
 constexpr int kFallbackCUs = 256;             // if the device cannot be queried
 constexpr int kMaxDevices = 64;
 
@@ -108,10 +109,14 @@ void clear_sched(pa::DecodeParams& a) {
 // largest power of two in [256, 4096] that still yields about four
 // work-groups per compute unit; once the (sequence, kv head) pairs alone give
 // that many, partitions only trim the tail left by the longest sequences and
-// are held at 1024 tokens. A split that would cut no more than a short tail
-// off the longest sequence is not worth its combine. The thresholds come
-// from a sweep of 128..4096-token partitions over the decode workloads.
-int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int cus) {
+// are held at 1024 tokens -- 2048 for 2-byte rows when that still splits the
+// longest context (the lognormal GQA batch: 275 against 283 us; its FP8
+// form, whose items carry the most arithmetic, 193 against 190 us, so FP8
+// keeps 1024). A split that would cut no more than a short tail off the
+// longest sequence is not worth its combine. The thresholds come from
+// sweeps of 128..4096-token partitions over the decode workloads.
+int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int cus,
+                   int kv_elem_bytes) {
   const int64_t items = (int64_t)num_seqs * num_kv_heads;
   const int64_t target = 4LL * cus;
   int P = kAutoMinPartition;
@@ -121,7 +126,11 @@ int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
       break;
     }
   }
-  if (items >= target && P > kAutoBalancedPartition) P = kAutoBalancedPartition;
+  if (items >= target && P > kAutoBalancedPartition) {
+    const bool wide = kv_elem_bytes >= 2 &&
+                      2LL * max_context_len > 3LL * kAutoBalancedPartitionWide;
+    P = wide ? kAutoBalancedPartitionWide : kAutoBalancedPartition;
+  }
   if (2LL * max_context_len <= 3LL * P) return -1;
   return P;
 }
@@ -205,8 +214,9 @@ int decode_impl(const void* q, const void* key_cache, const void* value_cache, b
 
   int cus = device_cu_count();
   if (cus <= 0) cus = kFallbackCUs;
-  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, max_context_len, cus)
-                                    : partition_size;
+  const int P = partition_size == 0
+                    ? auto_partition(num_seqs, num_kv_heads, max_context_len, cus, fp8_cache ? 1 : 2)
+                    : partition_size;
   const bool split = P > 0;
 
   pa::DecodeParams a;
@@ -275,7 +285,7 @@ CascadePlan cascade_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t block_s
   c.prefix_len = shared_prefix_blocks * block_size;
   c.suffix_max = max_context_len > c.prefix_len ? max_context_len - c.prefix_len : 0;
   int P = partition_size;
-  if (P == 0) P = auto_partition(num_seqs, num_kv_heads, c.suffix_max, cus);
+  if (P == 0) P = auto_partition(num_seqs, num_kv_heads, c.suffix_max, cus, 2);
   if (P < 0) P = (int32_t)((c.suffix_max + 31) / 32 * 32);   // one partition
   if (P <= 0) P = 32;                                           // no suffix at all
   c.part_tokens = P;
@@ -441,11 +451,13 @@ int pa_cache_write_fp8(const void* k, const void* v, void* key_cache, void* valu
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                 int32_t max_context_len, int32_t num_cus) {
+                                 int32_t max_context_len, int32_t cache_elem_bytes,
+                                 int32_t num_cus) {
   if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0) return 0;
+  if (cache_elem_bytes != 1 && cache_elem_bytes != 2) return 0;
   int cus = num_cus > 0 ? num_cus : device_cu_count();
   if (cus <= 0) cus = kFallbackCUs;
-  return auto_partition(num_seqs, num_kv_heads, max_context_len, cus);
+  return auto_partition(num_seqs, num_kv_heads, max_context_len, cus, cache_elem_bytes);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_size,

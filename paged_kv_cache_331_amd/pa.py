@@ -34,7 +34,7 @@ SIGNATURES = {
     "pa_cache_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
                                       _i32, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_cache_write_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
@@ -179,9 +179,11 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, head_size: int,
 
 
 def decode_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int,
-                          num_cus: int = 0) -> int:
-    """Tokens per partition of the automatic split (-1: single pass)."""
-    return int(load().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, num_cus))
+                          cache_elem_bytes: int = 2, num_cus: int = 0) -> int:
+    """Tokens per partition of the automatic split (-1: single pass); cache_elem_bytes
+    is 2 for pa_decode / the cascade, 1 for an FP8 cache."""
+    return int(load().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
+                                               cache_elem_bytes, num_cus))
 
 
 def decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

@@ -152,23 +152,28 @@ def test_slot_mapping_validation(lib, args, code):
     assert pa.load().pa_decode_slot_mapping(bt, mb, lens, n, bs, out, None) == code
 
 
-@pytest.mark.parametrize("B,Hkv,maxlen,cus,expect", [
-    (64, 32, 2046, 256, 1024),     # MHA batch: enough pairs, split held at 1024 tokens
-    (256, 8, 4096, 256, 1024),     # GQA batch with a lognormal length tail
-    (128, 8, 1536, 256, -1),       # longest context within 1.5 partitions: single pass
-    (4, 8, 93064, 256, 2048),      # long contexts: largest split with >= 4 WGs per CU
-    (4, 4, 99, 256, -1),           # tiny batch
-    (1, 8, 8192, 256, 256),        # too few pairs for the target: smallest partition
-    (4, 8, 93064, 64, 4096),       # a smaller device needs fewer work-groups
-    (0, 8, 0, 256, -1),
+@pytest.mark.parametrize("B,Hkv,maxlen,esz,cus,expect", [
+    (64, 32, 2046, 2, 256, 1024),  # MHA batch: enough pairs, split held at 1024 tokens
+    (64, 32, 2046, 1, 256, 1024),  # its FP8 form
+    (256, 8, 4096, 2, 256, 2048),  # GQA batch, 2-byte rows, lognormal tail past 3072 tokens
+    (256, 8, 4096, 1, 256, 1024),  # its FP8 form stays at 1024
+    (256, 8, 3072, 2, 256, 1024),  # 2048 would not split the longest context
+    (128, 8, 1536, 2, 256, -1),    # longest context within 1.5 partitions: single pass
+    (4, 8, 93064, 2, 256, 2048),   # long contexts: largest split with >= 4 WGs per CU
+    (4, 8, 93064, 1, 256, 2048),
+    (4, 4, 99, 2, 256, -1),        # tiny batch
+    (1, 8, 8192, 2, 256, 256),     # too few pairs for the target: smallest partition
+    (4, 8, 93064, 2, 64, 4096),    # a smaller device needs fewer work-groups
+    (0, 8, 0, 2, 256, -1),
 ])
-def test_auto_partition_rule(lib, B, Hkv, maxlen, cus, expect):
-    assert pa.decode_partition_size(B, Hkv, maxlen, cus) == expect
+def test_auto_partition_rule(lib, B, Hkv, maxlen, esz, cus, expect):
+    assert pa.decode_partition_size(B, Hkv, maxlen, esz, cus) == expect
 
 
 def test_auto_partition_invalid(lib):
-    assert pa.decode_partition_size(-1, 8, 10, 256) == 0
-    assert pa.decode_partition_size(1, 0, 10, 256) == 0
+    assert pa.decode_partition_size(-1, 8, 10, 2, 256) == 0
+    assert pa.decode_partition_size(1, 0, 10, 2, 256) == 0
+    assert pa.decode_partition_size(1, 8, 10, 4, 256) == 0
 
 
 def _decode_fp8(**kw):

@@ -46,7 +46,8 @@ def _persistent_expected(b, P: int) -> bool:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     spec = b.spec
     if P == 0:
-        P = pa.decode_partition_size(b.num_seqs, spec.num_kv_heads, b.max_context_len)
+        P = pa.decode_partition_size(b.num_seqs, spec.num_kv_heads, b.max_context_len,
+                                     1 if b.cache_dtype == "fp8" else 2)
     if P < 0:
         return False
     parts = -(-b.max_context_len // P)

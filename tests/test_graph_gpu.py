@@ -1,7 +1,8 @@
 """GPU: the hot path captured in a HIP graph and replayed.
 
-A decode step (slot of the new token, cache write, attention) and a prefill
-step are captured once through torch.cuda.graph and replayed several times,
+A decode step (slot of the new token, cache write, attention; as three calls
+and as one pa_decode_append call) and a prefill step are captured once
+through torch.cuda.graph and replayed several times,
 with unrelated eager work and synchronisations between the replays. Every
 replay must give the eager result bitwise. The library enqueues kernels only
 (no memset, no allocation, no host synchronisation), and the persistent
@@ -38,8 +39,18 @@ def _eager_noise():
     return float((x * 2).sum().item())
 
 
-def _decode_step(b, d, out, slots, ws, P, cascade):
+def _decode_step(b, d, out, slots, ws, P, cascade, append=False):
     bs = b.spec.block_size
+    if append:
+        if b.cache_dtype == "fp8":
+            pa.decode_append_fp8(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens, float(b.scale),
+                                 float(b.k_scale), float(b.v_scale), b.max_context_len, out=out,
+                                 slot_mapping=slots, partition_size=P, workspace=ws)
+        else:
+            pa.decode_append(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens, float(b.scale),
+                             b.max_context_len, b.spec.shared_prefix_blocks if cascade else 0,
+                             out=out, slot_mapping=slots, partition_size=P, workspace=ws)
+        return
     pa.decode_slot_mapping(d.bt, d.lens, bs, out=slots)
     if b.cache_dtype == "fp8":
         pa.cache_write_fp8(d.k_new, d.v_new, d.kc, d.vc, slots, float(b.k_scale),
@@ -58,16 +69,24 @@ def _decode_step(b, d, out, slots, ws, P, cascade):
 
 
 CASES = [
-    ("mha_persistent", dataclasses.replace(wl.CONFIGS["llama2_7b_mha"], num_seqs=8), 1024, False),
-    ("gqa", wl.small_variant("gqa_8b", 32), 0, False),
-    ("fp8_mha", dataclasses.replace(wl.CONFIGS["llama2_7b_mha_fp8"], num_seqs=8), 1024, False),
+    ("mha_persistent", dataclasses.replace(wl.CONFIGS["llama2_7b_mha"], num_seqs=8), 1024, False,
+     False),
+    ("gqa", wl.small_variant("gqa_8b", 32), 0, False, False),
+    ("fp8_mha", dataclasses.replace(wl.CONFIGS["llama2_7b_mha_fp8"], num_seqs=8), 1024, False,
+     False),
     ("cascade", dataclasses.replace(wl.CONFIGS["prefix_shared_write"], num_seqs=32, len_hi=2500),
-     1024, True),
+     1024, True, False),
+    ("append_mha_persistent", dataclasses.replace(wl.CONFIGS["llama2_7b_mha"], num_seqs=8), 1024,
+     False, True),
+    ("append_gqa", wl.small_variant("gqa_8b", 32), 0, False, True),
+    ("append_fp8_gqa", wl.small_variant("gqa_8b_fp8", 32), 0, False, True),
+    ("append_cascade", dataclasses.replace(wl.CONFIGS["prefix_shared_write"], num_seqs=32,
+                                           len_hi=2500), 1024, True, True),
 ]
 
 
-@pytest.mark.parametrize("name,spec,P,cascade", CASES, ids=[c[0] for c in CASES])
-def test_decode_step_graph_replays(name, spec, P, cascade):
+@pytest.mark.parametrize("name,spec,P,cascade,append", CASES, ids=[c[0] for c in CASES])
+def test_decode_step_graph_replays(name, spec, P, cascade, append):
     b = wl.make_batch(spec)
     d = Device(b)
     Hq, D = spec.num_q_heads, spec.head_size
@@ -85,21 +104,25 @@ def test_decode_step_graph_replays(name, spec, P, cascade):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for _ in range(2):
-            _decode_step(b, d, out, slots, ws, P, cascade)
+            _decode_step(b, d, out, slots, ws, P, cascade, append)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     ref = out.clone()
     ref_k = d.kc.clone()
+    ref_v = d.vc.clone()
+    ref_slots = slots.clone()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _decode_step(b, d, out, slots, ws, P, cascade)
+        _decode_step(b, d, out, slots, ws, P, cascade, append)
     for r in range(REPLAYS):
         out.fill_(0)
+        slots.fill_(-7)
         g.replay()
         torch.cuda.synchronize()
         assert _same(out, ref), f"replay {r}"
-        assert _same(d.kc, ref_k)
+        assert _same(d.kc, ref_k) and _same(d.vc, ref_v)
+        assert torch.equal(slots, ref_slots)
         _eager_noise()
         torch.cuda.synchronize()
 

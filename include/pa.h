@@ -327,10 +327,12 @@ PA_API int pa_decode_cascade(const void* q, const void* key_cache, const void* v
  *   pa_decode_slot_mapping(block_tables, ..., slot_mapping);
  *   pa_cache_write(k, v, key_cache, value_cache, slot_mapping, num_seqs, ...);
  *   pa_decode_cascade(q, key_cache, value_cache, ..., shared_prefix_blocks, ...);
- * (pa_decode when shared_prefix_blocks == 0): the same cache contents and the
- * same output bits, with no separate slot or write launch. The work-group
+ * (pa_decode when shared_prefix_blocks == 0), with no separate slot or write
+ * launch: the same slots and cache contents bit for bit, and the same output
+ * up to rounding order (the new token's term is summed last, so the last
+ * bits may differ; both are held to the decode tolerance). The work-group
  * that attends over position L - 1 of kv head g stores that head's k/v row
- * at the slot and uses the stored value as the row of that position.
+ * at the slot and attends over the same row values, taken from k / v.
  * k, v         : [num_seqs, num_kv_heads, head_size] (device), dtype of q,
  *                16-byte aligned
  * slot_mapping : int32 [num_seqs] (device, written) -- the slot of position

@@ -30,6 +30,13 @@
 //    becomes -inf and the V row is replaced by zeros, so whatever those slots
 //    hold (even NaN) cannot reach the result. Table entries past the last
 //    block are never read.
+//  * Write-then-attend (the book's §4 decode phase: the new token's k/v go to
+//    the next slot of the last block, then attention covers it too), when
+//    the call appends: the item holding position L-1 reads the cached
+//    positions before it and takes the new token from k_new / v_new as one
+//    more tile, on the wave that would take the next tile; that wave's row-0
+//    lanes also store the row at its slot. The slot is never read in the
+//    same launch, so the store needs no ordering against any load.
 #include <type_traits>
 
 #include "pa_device.h"

@@ -264,7 +264,7 @@ PA_API int pa_decode_fp8(const void* q, const void* key_cache, const void* value
  * pa_decode_cascade_workspace_size -- workspace bytes of pa_decode_cascade.
  *
  * 256 bytes of scheduler state, and room for the fp32 partials of
- * ceil(prefix_len / 128) prefix chunks plus the partitions of the positions
+ * ceil(prefix_len / 256) prefix chunks plus the partitions of the positions
  * past the prefix (as pa_decode_workspace_size counts them for
  * max_context_len - prefix_len tokens), per (sequence, query head), with
  * prefix_len = shared_prefix_blocks * block_size. With

@@ -85,8 +85,14 @@ uint32_t sched_tag(const void* workspace) {
 // the dequantisation shared by the group makes the kernel VALU-heavy and the
 // one-per-item grid keeps more waves resident, and for partitions of 512
 // tokens or fewer (16384+ items: 10-50% slower).
-constexpr int kPersistWgsPerCu = 2;
-constexpr int kPersistWgsPerCuFp8 = 3;
+#ifndef PA_PERSIST_WGS_PER_CU
+#define PA_PERSIST_WGS_PER_CU 2
+#endif
+#ifndef PA_PERSIST_WGS_PER_CU_FP8
+#define PA_PERSIST_WGS_PER_CU_FP8 3
+#endif
+constexpr int kPersistWgsPerCu = PA_PERSIST_WGS_PER_CU;
+constexpr int kPersistWgsPerCuFp8 = PA_PERSIST_WGS_PER_CU_FP8;
 constexpr int kPersistMinPartition = 1024;
 constexpr int64_t kPersistMaxItems = 8192;
 

@@ -99,7 +99,7 @@ hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
 // Keys of the shared prefix one cascade work-group covers, and the shape of
 // that work-group: waves, and 16-row blocks per wave.
 #ifndef PA_PREFIX_CHUNK
-#define PA_PREFIX_CHUNK 128
+#define PA_PREFIX_CHUNK 256
 #endif
 #ifndef PA_CASCADE_WAVES
 #define PA_CASCADE_WAVES 8

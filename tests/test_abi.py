@@ -231,9 +231,9 @@ def test_fp8_zero_work_is_ok(lib):
 def test_cascade_workspace_arithmetic(lib):
     ws = pa.load().pa_decode_cascade_workspace_size
     al = lambda x: (x + 255) // 256 * 256
-    # 128 sequences x 32 heads; prefix 32 blocks of 32 = 1024 tokens -> 8 chunks of 128;
-    # suffix up to 1536 - 1024 = 512 tokens in partitions of 256 -> 2; 10 slots
-    n = 128 * 32 * 10
+    # 128 sequences x 32 heads; prefix 32 blocks of 32 = 1024 tokens -> 4 chunks of 256;
+    # suffix up to 1536 - 1024 = 512 tokens in partitions of 256 -> 2; 6 slots
+    n = 128 * 32 * 6
     assert ws(128, 32, 128, 32, 1536, 32, 256) == 256 + 2 * al(4 * n) + al(4 * n * 128)
     assert ws(128, 32, 128, 32, 1536, 0, 256) == pa.load().pa_decode_workspace_size(
         128, 32, 128, 1536, 256)

@@ -223,6 +223,28 @@ def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 20) -> dict:
     return {"bytes": nbytes, "GBs": 2 * nbytes / t / 1e9, "ms": t * 1e3}
 
 
+def cold_calls(step, reps: int = 20, flush_bytes: int = 1 << 30) -> list:
+    """Event-timed calls, each after a read of a ``flush_bytes`` buffer.
+
+    The read (outside the event pair) replaces the L2 and last-level cache
+    contents with clean lines of another buffer, so the timed call finds none
+    of its own bytes there and writes nothing back: HBM-cold numbers, beside
+    the back-to-back steps of the main loop. Returns milliseconds per call.
+    """
+    import torch
+    buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    evs = []
+    for _ in range(reps):
+        buf.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        step(e0, e1)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del buf
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix peak, AMD's published figure
 PREFILL_METRIC = "prefill tokens/s + TFLOP/s (% of MI355X dense fp16/bf16 MFMA peak), 1 GPU"
 
@@ -481,6 +503,7 @@ def main(argv=None) -> int:
           f" (median {np.median(dec_ms):.4f}, min {np.min(dec_ms):.4f}, max {np.max(dec_ms):.4f})",
           file=sys.stderr, flush=True)
 
+    cold_ms = cold_calls(step)
     copy = copy_bandwidth()
     nbytes = algorithmic_bytes(spec, batch.context_lens)
     # A block shared by many tables must come from HBM at least once, so the
@@ -541,7 +564,13 @@ def main(argv=None) -> int:
             "bytes_per_token_per_kv_head": nbytes["per_token_head"],
             "decode_ms_mean": decode_ms, "decode_ms_median": float(np.median(dec_ms)),
             "decode_ms_min": float(np.min(dec_ms)),
-            "measured_copy_GBs": copy["GBs"], "frac_of_copy": achieved / copy["GBs"]},
+            "measured_copy_GBs": copy["GBs"], "frac_of_copy": achieved / copy["GBs"],
+            "cold": {"flush": "1 GiB read before each call, outside the events",
+                     "calls": len(cold_ms), "ms_mean": float(np.mean(cold_ms)),
+                     "ms_median": float(np.median(cold_ms)),
+                     "GBs": (nbytes["total_unique"] + app) / (float(np.mean(cold_ms)) * 1e-3) / 1e9,
+                     "frac": (nbytes["total_unique"] + app) / (float(np.mean(cold_ms)) * 1e-3)
+                             / 1e9 / PEAK_HBM_GBS}},
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

@@ -2,9 +2,11 @@
 """Decode-attention benchmark on one MI355X.
 
 One step is one pass of the whole decode hot path over a synthetic batch
-already resident in HBM: the newest token's slot (pa_decode_slot_mapping),
-the cache write of its k/v (pa_cache_write), then paged attention over every
-cached position (pa_decode, automatic single-pass / split-K choice).
+already resident in HBM: the newest token's slot, the cache write of its k/v,
+then paged attention over every cached position (automatic single-pass /
+split-K choice). By default the step is one pa_decode_append call (the cascade
+form for a batch whose tables share a prefix, the FP8 form for an FP8 cache);
+--separate times it as pa_decode_slot_mapping + pa_cache_write + pa_decode.
 
 Default workload: the Llama-2-7B-shaped single-layer decode batch (64
 sequences, 32 query = 32 kv heads, head size 128, block size 16, fp16,
@@ -12,9 +14,12 @@ context lengths uniform in [512, 2048], shuffled block tables over a pool of
 the blocks used plus 10%).
 
 Prints ONE JSON line: tokens/s for the whole job (one new token per sequence
-per step), the decode kernel's achieved HBM bandwidth against MI355X's 8 TB/s
+per step), the decode call's achieved HBM bandwidth against MI355X's 8 TB/s
 peak (from HIP events recorded on the launch stream inside the timed
-region), and the fp64 CPU oracle timed on a bounded sample of the same batch.
+region), the counter-measured HBM traffic per call when profiles/ holds it
+for these kernel sources, the same call timed HBM-cold (after a cache flush,
+outside the timed region), and the fp64 CPU oracle timed on a bounded sample
+of the same batch.
 """
 from __future__ import annotations
 

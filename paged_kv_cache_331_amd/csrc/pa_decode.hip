@@ -94,7 +94,16 @@ __device__ __forceinline__ void append_row(const DecodeParams& a, int s, int g, 
 constexpr float kEmptyMax = -1.0e30f;  // running max before any token: finite, so
                                        // exp2(m_old - m_new) never sees inf - inf
 constexpr float kSlack = 8.f;              // lazy softmax reference: weights stay <= 2^8
-constexpr int kTile = 16;                  // tokens per wave iteration
+// Tokens per wave iteration: 16, or 8 in the one-work-group-per-item kernel
+// for partitions of at most kShortPartition tokens over a 2-byte cache at
+// head size 128 (a tile is always at least two load rows). Short items are
+// latency-bound; the half tiles measured 50.1-50.8 us against 51.9-53.1 on
+// the cascade's suffix items and within noise on short partitions of the
+// MHA and GQA batches, and 8-16% slower on long partitions, so only short
+// partitions take them.
+constexpr int kTileTokens = 16;
+constexpr int kShortTileTokens = 8;
+constexpr int kShortPartition = 512;
 constexpr int kTableChunk = 256;           // table entries staged per LDS pass
 
 union Vec16 {
@@ -112,7 +121,8 @@ struct DecodeLds {
 // work-group (every thread takes the same path and the same barriers).
 // APP: the call appends each sequence's new token (write-then-attend);
 // instantiated separately so that a plain decode carries none of its code.
-template <class DT, class KT, int D, int G, bool APP>
+// TILE: tokens per wave iteration (raised to two load rows if smaller).
+template <class DT, class KT, int D, int G, bool APP, int TILE>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
                                             DecodeLds<D, G>& sm) {
   using S = Storage<DT>;
@@ -123,6 +133,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   constexpr int NW = kDecodeWaves;
   constexpr int LPR = D / DL;          // lanes per token row
   constexpr int ROWS = 64 / LPR;       // token rows per load instruction
+  constexpr int kTile = TILE > 2 * ROWS ? TILE : 2 * ROWS;   // tokens per wave iteration
   constexpr int TG = kTile / ROWS;     // load instructions per tile and tensor
   static_assert(TG % 2 == 0, "p.V pairs rows tg, tg+1");
   constexpr int NT = NW * 64;
@@ -457,7 +468,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 // the grid. With few pairs (long contexts) the sequence index comes last, so
 // one sequence's partitions run together; each order measured faster in its
 // regime.
-template <class DT, class KT, int D, int G, bool APP>
+template <class DT, class KT, int D, int G, bool APP, int TILE>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
   int wg = blockIdx.x;
@@ -465,7 +476,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   wg /= a.num_kv_heads;
   const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
   const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
-  decode_item<DT, KT, D, G, APP>(a, g, s, p, sm);
+  decode_item<DT, KT, D, G, APP, TILE>(a, g, s, p, sm);
 }
 
 // Persistent grid: gridDim.x (at most the item count) work-groups walk the
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int g = it % Hkv;
     const int s = (it / Hkv) % a.num_seqs;
     const int p = it / (Hkv * a.num_seqs);
-    decode_item<DT, KT, D, G, APP>(a, g, s, p, sm);
+    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
     if (!counted) {
       item += grid;
       continue;
@@ -680,8 +691,17 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
-    hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP>), dim3((uint32_t)nwg),
-                       dim3(kDecodeWaves * 64), 0, st, b);
+    bool short_tiles = false;
+    if constexpr (D == 128 && std::is_same<KT, DT>::value)
+      short_tiles = a.part_tokens <= kShortPartition;
+    if (short_tiles) {
+      if constexpr (D == 128 && std::is_same<KT, DT>::value)
+        hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kShortTileTokens>),
+                           dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
+    } else {
+      hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kTileTokens>),
+                         dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
+    }
     if (!combine) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

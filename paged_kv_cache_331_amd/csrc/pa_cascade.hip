@@ -18,7 +18,7 @@
 // softmax weights fed to the matrix cores).
 //
 // Prefix kernel layout: one work-group (cascade_waves(D) waves of
-// kCascadeRowBlocks 16-row blocks: 8 x 1 at head size 128, 4 x 1 at 64) per
+// kCascadeRowBlocks 16-row blocks: 4 x 1 at both head sizes) per
 // (kv head, row tile, chunk of kPrefixChunk prefix keys), on the matrix-core
 // attention core of pa_mq.h. Rows are (sequence, query head) pairs of the kv
 // head; each row's keys end at min(L, prefix_len), and the work-group writes

@@ -102,7 +102,7 @@ hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
 #define PA_PREFIX_CHUNK 256
 #endif
 #ifndef PA_CASCADE_WAVES
-#define PA_CASCADE_WAVES 8
+#define PA_CASCADE_WAVES 4
 #endif
 #ifndef PA_CASCADE_ROW_BLOCKS
 #define PA_CASCADE_ROW_BLOCKS 1

@@ -169,7 +169,8 @@ PA_API size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, in
  * rule: the largest power of two in [256, 4096] that still gives about four
  * work-groups per compute unit; when the (sequence, kv head) pairs alone
  * give that many, at most 1024 -- or 2048 for 2-byte elements when the
- * longest context exceeds 3072 tokens; no split when the longest context is
+ * longest context exceeds 3072 tokens, 1536 for 1-byte elements when it
+ * exceeds 2304; no split when the longest context is
  * at most 1.5 partitions. num_cus <= 0 asks the current HIP device for its
  * compute-unit count (256 if it cannot be queried). Pure host arithmetic
  * otherwise; no device work is enqueued. Returns 0 for invalid sizes

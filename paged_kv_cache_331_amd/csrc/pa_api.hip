@@ -15,6 +15,7 @@ constexpr int kAutoMinPartition = 256;       // partition sizes an automatic cho
 constexpr int kAutoMaxPartition = 4096;
 constexpr int kAutoBalancedPartition = 1024;  // cap when the batch alone fills the chip
 constexpr int kAutoBalancedPartitionWide = 2048;  // the same cap for 2-byte rows and long tails
+constexpr int kAutoBalancedPartitionFp8 = 1536;   // the same cap for FP8 rows and long tails
 constexpr int kFallbackCUs = 256;             // if the device cannot be queried
 constexpr int kMaxDevices = 64;
 
@@ -115,10 +116,10 @@ void clear_sched(pa::DecodeParams& a) {
 // largest power of two in [256, 4096] that still yields about four
 // work-groups per compute unit; once the (sequence, kv head) pairs alone give
 // that many, partitions only trim the tail left by the longest sequences and
-// are held at 1024 tokens -- 2048 for 2-byte rows when that still splits the
-// longest context (the lognormal GQA batch: 275 against 283 us; its FP8
-// form, whose items carry the most arithmetic, 193 against 190 us, so FP8
-// keeps 1024). A split that would cut no more than a short tail off the
+// are held at 1024 tokens -- 2048 for 2-byte rows and 1536 for FP8 rows when
+// that still splits the longest context (the lognormal GQA batch: 275
+// against 283 us at 2048; its FP8 form 177-180 against 186-188 us at 1536,
+// and 193 at 2048). A split that would cut no more than a short tail off the
 // longest sequence is not worth its combine. The thresholds come from
 // sweeps of 128..4096-token partitions over the decode workloads.
 int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int cus,
@@ -133,9 +134,8 @@ int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
     }
   }
   if (items >= target && P > kAutoBalancedPartition) {
-    const bool wide = kv_elem_bytes >= 2 &&
-                      2LL * max_context_len > 3LL * kAutoBalancedPartitionWide;
-    P = wide ? kAutoBalancedPartitionWide : kAutoBalancedPartition;
+    const int wide = kv_elem_bytes >= 2 ? kAutoBalancedPartitionWide : kAutoBalancedPartitionFp8;
+    P = 2LL * max_context_len > 3LL * wide ? wide : kAutoBalancedPartition;
   }
   if (2LL * max_context_len <= 3LL * P) return -1;
   return P;

@@ -156,7 +156,8 @@ def test_slot_mapping_validation(lib, args, code):
     (64, 32, 2046, 2, 256, 1024),  # MHA batch: enough pairs, split held at 1024 tokens
     (64, 32, 2046, 1, 256, 1024),  # its FP8 form
     (256, 8, 4096, 2, 256, 2048),  # GQA batch, 2-byte rows, lognormal tail past 3072 tokens
-    (256, 8, 4096, 1, 256, 1024),  # its FP8 form stays at 1024
+    (256, 8, 4096, 1, 256, 1536),  # its FP8 form: 1536
+    (256, 8, 2304, 1, 256, 1024),  # FP8, 1536 would not split the longest context
     (256, 8, 3072, 2, 256, 1024),  # 2048 would not split the longest context
     (128, 8, 1536, 2, 256, -1),    # longest context within 1.5 partitions: single pass
     (4, 8, 93064, 2, 256, 2048),   # long contexts: largest split with >= 4 WGs per CU

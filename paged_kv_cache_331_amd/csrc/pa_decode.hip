@@ -14,7 +14,8 @@
 //    every K/V row is fetched from HBM once per step.
 //  * The partition's block-table entries are staged once into LDS; each wave
 //    reads the block id of its tile from LDS and makes it wave-uniform.
-//  * A wave walks 16-token tiles. Lanes form "token rows"; each lane holds
+//  * A wave walks 16-token tiles (8-token tiles for short partitions of a
+//    2-byte cache at head size 128). Lanes form "token rows"; each lane holds
 //    16 bytes of one token (8 dimensions of a 2-byte cache, 16 of an FP8 one
 //    at head size 128), so one load instruction reads whole K or V rows of
 //    4, 8 or 16 consecutive slots. Whole rows per instruction and

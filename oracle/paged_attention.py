@@ -131,21 +131,30 @@ def _softmax_attend(qv: np.ndarray, K: np.ndarray, V: np.ndarray,
     return p @ V, p
 
 
-def decode_one(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
-               block_tables: np.ndarray, context_lens: np.ndarray, scale,
-               dtype: str, seq: int, head: int, cache_dtype: Optional[str] = None,
-               k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
-    """Output row ``out[seq, head, :]`` in float64."""
+def _row_operands(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                  block_tables: np.ndarray, context_lens: np.ndarray, dtype: str,
+                  seq: int, head: int, cache_dtype: Optional[str], k_scale: float,
+                  v_scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """q row, and the K / V rows of positions < L of its kv head, as float64."""
     cdt = cache_dtype or dtype
     Hq = q.shape[1]
     Hkv = key_cache.shape[2]
     g = head // (Hq // Hkv)
     L = int(context_lens[seq])
-    if L == 0:
-        return np.zeros(q.shape[2], dtype=np.float64)
     K = gather_positions(key_cache, block_tables[seq], L, g, cdt, k_scale)
     V = gather_positions(value_cache, block_tables[seq], L, g, cdt, v_scale)
-    qv = to_float64(q[seq, head], dtype)
+    return to_float64(q[seq, head], dtype), K, V
+
+
+def decode_one(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+               block_tables: np.ndarray, context_lens: np.ndarray, scale,
+               dtype: str, seq: int, head: int, cache_dtype: Optional[str] = None,
+               k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Output row ``out[seq, head, :]`` in float64."""
+    if int(context_lens[seq]) == 0:
+        return np.zeros(q.shape[2], dtype=np.float64)
+    qv, K, V = _row_operands(q, key_cache, value_cache, block_tables, context_lens, dtype,
+                             seq, head, cache_dtype, k_scale, v_scale)
     out, _ = _softmax_attend(qv, K, V, float(np.float32(scale)))
     return out
 
@@ -182,18 +191,20 @@ def decode(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
     return out
 
 
-def attention_weights(q: np.ndarray, key_cache: np.ndarray, block_tables: np.ndarray,
-                      context_lens: np.ndarray, scale, dtype: str,
-                      seq: int, head: int) -> np.ndarray:
-    """Softmax weights over positions < L for one (sequence, query head)."""
-    Hq = q.shape[1]
-    Hkv = key_cache.shape[2]
-    g = head // (Hq // Hkv)
-    L = int(context_lens[seq])
-    K = gather_positions(key_cache, block_tables[seq], L, g, dtype)
-    logits = float(np.float32(scale)) * (K @ to_float64(q[seq, head], dtype))
-    w = np.exp(logits - logits.max())
-    return w / w.sum()
+def attention_weights(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
+                      block_tables: np.ndarray, context_lens: np.ndarray, scale, dtype: str,
+                      seq: int, head: int, cache_dtype: Optional[str] = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """The softmax weights over positions < L that :func:`decode_one` applies
+    to the V rows of one (sequence, query head): the same gathered operands
+    and the same ``_softmax_attend`` call, so ``weights @ V`` is that output
+    row. Empty for L == 0."""
+    if int(context_lens[seq]) == 0:
+        return np.zeros(0, dtype=np.float64)
+    qv, K, V = _row_operands(q, key_cache, value_cache, block_tables, context_lens, dtype,
+                             seq, head, cache_dtype, k_scale, v_scale)
+    _, p = _softmax_attend(qv, K, V, float(np.float32(scale)))
+    return p
 
 
 def decode_partitioned(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,

@@ -285,10 +285,94 @@ def test_weights_sum_to_one(name):
     b = wl.make_batch(spec)
     for s in range(b.num_seqs):
         for h in range(spec.num_q_heads):
-            p = oracle.attention_weights(b.q, b.key_cache, b.block_tables, b.context_lens,
-                                         b.scale, b.dtype, s, h)
+            p = oracle.attention_weights(b.q, b.key_cache, b.value_cache, b.block_tables,
+                                         b.context_lens, b.scale, b.dtype, s, h)
             assert p.shape == (int(b.context_lens[s]),)
             assert abs(p.sum() - 1.0) <= 1e-14 and np.all(p >= 0)
+
+
+def _bruteforce_weights(c, s, h):
+    """Weights of one (sequence, head) by explicit loops over tokens, flat-slot
+    addressing and scipy's softmax (independent of the oracle's gather)."""
+    q = _torch_upcast(c["q"], c["dtype"])
+    kc = _torch_upcast(c["key_cache"], c["dtype"])
+    NB, bs, Hkv, D = kc.shape
+    kflat = kc.reshape(NB * bs, Hkv, D)
+    g = h // (q.shape[1] // Hkv)
+    L = int(c["context_lens"][s])
+    logits = []
+    for t in range(L):
+        slot = int(c["block_tables"][s][t // bs]) * bs + (t % bs)
+        logits.append(float(c["scale"]) * float(kflat[slot, g] @ q[s, h]))
+    return scipy.special.softmax(np.array(logits))
+
+
+def pin_weights_bruteforce(weights_fn, seed=5):
+    """P5b: the weights equal brute-force softmax weights, position by position,
+    and weights @ (brute-force gathered V) is the brute-force output row."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for (B, Hkv, G, D, bs, dtype) in [(3, 2, 2, 8, 4, "fp16"), (2, 1, 4, 4, 2, "bf16"),
+                                      (2, 2, 1, 8, 16, "fp16"), (2, 2, 4, 8, 4, "bf16")]:
+        lens = rng.integers(1, 40, size=B).tolist()
+        c = _random_case(rng, B, Hkv, G, D, bs, lens, dtype)
+        bf_out = _bruteforce(c)
+        vc = _torch_upcast(c["value_cache"], c["dtype"])
+        vflat = vc.reshape(-1, Hkv, D)
+        for s in range(B):
+            for h in range(Hkv * G):
+                p = weights_fn(c["q"], c["key_cache"], c["value_cache"], c["block_tables"],
+                               c["context_lens"], c["scale"], c["dtype"], s, h)
+                ref = _bruteforce_weights(c, s, h)
+                if p.shape != ref.shape or not np.allclose(p, ref, rtol=0, atol=1e-15):
+                    return False
+                L = int(c["context_lens"][s])
+                V = np.array([vflat[int(c["block_tables"][s][t // bs]) * bs + t % bs, h // G]
+                              for t in range(L)])
+                ok &= np.allclose(p @ V, bf_out[s, h], rtol=0, atol=1e-13)
+    return ok
+
+
+def test_weights_match_bruteforce():
+    assert pin_weights_bruteforce(oracle.attention_weights)
+
+
+def test_weights_are_decodes_weights():
+    """weights @ V of the oracle's own gather is the oracle's decode row (both
+    come from one computation), on a small draw of every workload shape."""
+    for name in wl.CONFIG_ORDER:
+        b = wl.make_batch(wl.small_variant(name, 2))
+        ref = oracle.decode(b.q, b.key_cache, b.value_cache, b.block_tables, b.context_lens,
+                            b.scale, b.dtype)
+        G = b.spec.num_q_heads // b.spec.num_kv_heads
+        for s in range(b.num_seqs):
+            for h in (0, b.spec.num_q_heads - 1):
+                p = oracle.attention_weights(b.q, b.key_cache, b.value_cache, b.block_tables,
+                                             b.context_lens, b.scale, b.dtype, s, h)
+                V = opa.gather_positions(b.value_cache, b.block_tables[s],
+                                         int(b.context_lens[s]), h // G, b.dtype)
+                assert np.array_equal(p @ V, ref[s, h])
+
+
+def _weights_mutant_head_map(q, kc, vc, bt, lens, scale, dtype, s, h):
+    Hkv = kc.shape[2]
+    G = q.shape[1] // Hkv
+    # query head h read kv head h % Hkv instead of h // G: swap to the head of that map
+    h2 = (h % Hkv) * G + (h // Hkv) % G
+    p = oracle.attention_weights(q[:, [h] * q.shape[1]], kc, vc, bt, lens, scale, dtype, s, h2)
+    return p
+
+
+@pytest.mark.parametrize("name", ["no_scale", "swapped_block_offset", "off_by_one_length",
+                                  "no_normalisation", "logit_sign", "wrong_gqa_head_map"])
+def test_weights_pin_catches_planted_mistake(name, monkeypatch):
+    """Each planted mistake, placed where the weights are computed, fails P5b."""
+    if name == "wrong_gqa_head_map":
+        fn = _weights_mutant_head_map
+    else:
+        MUTANTS[name](monkeypatch)
+        fn = opa.attention_weights
+    assert not pin_weights_bruteforce(fn)
 
 
 def test_book_figure_slots():

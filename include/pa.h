@@ -218,14 +218,21 @@ PA_API int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
  * workspace : device buffer, 256-byte aligned, of at least
  *             pa_decode_workspace_size(...) bytes for the same sizes and
  *             partition_size (may be NULL when that size is 0). Its contents
- *             need no initialisation. Its first 256 bytes carry
- *             scheduler state from one split call to the next on the same
- *             buffer (a 64-bit word: a tag in bytes 0-3, a work counter that
- *             every call returns to zero in bytes 4-7); a call that finds no
- *             such state (a fresh buffer, or one overwritten since) gives
- *             the same result with a fixed schedule. The rest is scratch
- *             for this call only. Calls that
- *             run at the same time need distinct workspaces.
+ *             need no initialisation. Its first 256 bytes carry scheduler
+ *             state from one split call to the next on the same buffer: a
+ *             64-bit word at offset 0 (a tag derived from the buffer's
+ *             address in bytes 0-3, a work counter in bytes 4-7) and a
+ *             32-bit finish count at offset 128. Every call that uses them
+ *             leaves (tag, 0) and 0 behind, also when only its partition
+ *             kernel ran, so a later call never starts from a used counter.
+ *             A call that finds no tag (a fresh buffer, or one overwritten
+ *             since) gives the same result with a fixed schedule. Between
+ *             calls the caller may reuse the buffer for anything, as long as
+ *             a write into bytes 4-7 or 128-131 also changes bytes 0-3
+ *             (any write of the whole head does): a counter or count changed
+ *             under an intact tag would make the next call skip work items.
+ *             The rest is scratch for this call only. Calls that run at the
+ *             same time need distinct workspaces.
  * Errors: PA_ERR_DTYPE; PA_ERR_SHAPE (non-positive head counts or sizes,
  * num_q_heads not a multiple of num_kv_heads, max_context_len above
  * max_blocks_per_seq * block_size, non-finite scale); PA_ERR_UNSUPPORTED

@@ -99,6 +99,7 @@ constexpr int64_t kPersistMaxItems = 8192;
 
 void set_sched(pa::DecodeParams& a, void* workspace, int cus, bool fp8_cache, int group) {
   a.sched = (unsigned long long*)workspace;
+  a.sched_done = (uint32_t*)((char*)workspace + pa::kSchedDoneOffset);
   a.sched_tag = sched_tag(workspace);
   const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
   const bool persist = !a.seq_major && (!fp8_cache || group == 1) &&
@@ -108,6 +109,7 @@ void set_sched(pa::DecodeParams& a, void* workspace, int cus, bool fp8_cache, in
 
 void clear_sched(pa::DecodeParams& a) {
   a.sched = nullptr;
+  a.sched_done = nullptr;
   a.sched_tag = 0;
   a.persist_grid = 0;
 }

@@ -485,13 +485,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
 // starts with item blockIdx.x; later items come from the counter half of the
 // scheduler word as grid + ticket, so a work-group that drew short items
 // takes more of them and none waits on a hardware dispatch slot. The counter
-// is trusted only when the word's tag half holds sched_tag, which the combine
-// kernel writes together with counter = 0 after every call; otherwise (the
+// is trusted only when the word's tag half holds sched_tag; otherwise (the
 // first call on a workspace) the items are walked with the fixed stride
 // gridDim.x. Every item is taken by exactly one work-group under either
-// schedule. One counter serves the whole chip: splitting it per XCD (each
-// XCD's work-groups on their own share of the items, with or without
-// stealing at the end) measured 3-9% slower.
+// schedule. The counter always returns to zero: on the counted walk the last
+// work-group to finish resets it (every ticket has been drawn by then), and
+// the combine kernel writes (tag, 0) after every call, which also arms the
+// counter after a fixed-stride walk. One counter serves the whole chip:
+// splitting it per XCD (each XCD's work-groups on their own share of the
+// items, with or without stealing at the end) measured 3-9% slower.
 template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
@@ -508,6 +510,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int p = it / (Hkv * a.num_seqs);
     decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
     if (!counted) {
+      // The next item writes its waves' sums into sm.part, which threads of
+      // this item may still be reading in the cross-wave merge: an item whose
+      // partition holds only the appended token meets no barrier before that
+      // write.
+      __syncthreads();
       item += grid;
       continue;
     }
@@ -521,6 +528,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     }
     __syncthreads();
     item = s_item[k];
+  }
+  // A work-group's last ticket (the one past the end) has been drawn. The
+  // grid-th work-group to get here is the last to draw: it returns the
+  // counter to zero and re-arms the finish count, so the next call finds
+  // (tag, 0) even if this call's combine kernel never runs.
+  if (counted && threadIdx.x == 0) {
+    if (atomicAdd(a.sched_done, 1u) == grid - 1) {
+      atomicExch(a.sched, (unsigned long long)a.sched_tag);
+      atomicExch(a.sched_done, 0u);
+    }
   }
 }
 
@@ -546,7 +563,10 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int tid = threadIdx.x;
   // The partition kernel has finished (stream order): leave the scheduler
   // state the next persistent launch on this workspace expects.
-  if (a.sched != nullptr && blockIdx.x == 0 && tid == 0) *a.sched = a.sched_tag;
+  if (a.sched != nullptr && blockIdx.x == 0 && tid == 0) {
+    *a.sched = a.sched_tag;
+    *a.sched_done = 0u;
+  }
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
   const int64_t oh = (int64_t)s * a.num_q_heads + h;
@@ -623,7 +643,10 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_few_kernel(const
   constexpr int CH = D / 4;                        // 16-byte chunks of one output row
   constexpr int HPW = kReduceThreads / CH;         // query heads per work-group
   const int tid = threadIdx.x;
-  if (a.sched != nullptr && blockIdx.x == 0 && tid == 0) *a.sched = a.sched_tag;
+  if (a.sched != nullptr && blockIdx.x == 0 && tid == 0) {
+    *a.sched = a.sched_tag;
+    *a.sched_done = 0u;
+  }
   const int hgroups = (a.num_q_heads + HPW - 1) / HPW;
   const int s = blockIdx.x / hgroups;
   const int h = (blockIdx.x % hgroups) * HPW + tid / CH;

@@ -45,12 +45,16 @@ struct DecodeParams {
   // Persistent scheduling (split calls whose combine kernel runs): the
   // partition kernel is launched with persist_grid work-groups that take the
   // (kv head, sequence, partition) items from the scheduler word *sched: low
-  // 32 bits a tag, high 32 bits a work counter. The combine kernel leaves it
-  // at (tag = sched_tag, counter = 0) for the next call; a partition kernel
-  // that finds another tag (a fresh or overwritten workspace) walks the items
-  // with a fixed stride instead. The tag sits at the lower address, so a
-  // write that reaches the counter from below clobbers the tag first.
+  // 32 bits a tag, high 32 bits a work counter. A partition kernel that
+  // finds another tag (a fresh or overwritten workspace) walks the items
+  // with a fixed stride and leaves the words alone; one that finds the tag
+  // draws tickets from the counter, and its last work-group to finish
+  // (counted in *sched_done) puts the word back to (tag, 0) and the count
+  // to 0. The combine kernel writes (tag, 0) and 0 after every call. The tag
+  // sits at the lowest address, so a write that reaches the counter from
+  // below clobbers the tag first.
   unsigned long long* sched;  // nullptr: one work-group per item
+  uint32_t* sched_done;       // work-groups of a counted walk that have finished
   uint32_t sched_tag;
   int32_t persist_grid;       // 0: one work-group per item
   // Write-then-attend in the same launch: each sequence's new token (position
@@ -64,9 +68,11 @@ struct DecodeParams {
   float v_scale_w = 1.f;
 };
 
-// Bytes reserved for the scheduler word at the head of a split-K workspace,
-// before the partials.
+// Bytes reserved for the scheduler words at the head of a split-K workspace,
+// before the partials: the (tag, counter) word at offset 0 and the finish
+// count at kSchedDoneOffset, in another 128-byte line.
 constexpr int kSchedBytes = 256;
+constexpr int kSchedDoneOffset = 128;
 
 // Work-groups of the partition kernel per launch: one per
 // (kv head, partition, sequence), or a persistent grid of a few per compute

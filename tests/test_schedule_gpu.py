@@ -225,3 +225,55 @@ def test_concurrent_calls_on_two_streams():
     for o1, o2 in outs:
         assert _same(o1, ref1) and _same(o2, ref2)
     assert _counter(ws[0]) == 0 and _counter(ws[1]) == 0
+
+
+def _done_count(ws: torch.Tensor) -> int:
+    """The finish count of a counted walk, 32 bits at byte offset 128."""
+    return int(ws[128:132].view(torch.int32).item())
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_mha", "llama2_7b_mha_fp8"])
+def test_append_new_token_only_partitions_both_schedules(name):
+    """Fused append on the persistent grid with lengths L = 1 (mod 1024), so
+    that some items' partitions hold only the new token and skip the table
+    loop (and its barriers). The first call on a random workspace walks the
+    items with the fixed stride, the next ones draw tickets: every call must
+    equal the oracle (whole pools bitwise, every output within the bar) and
+    the calls must be bitwise equal to each other."""
+    lens = [1025, 2049, 1, 1024, 1026, 2048, 1537, 1025]
+    spec = wl.small_variant(name, len(lens))
+    b = wl.make_batch(spec, lengths=lens)
+    P = 1024
+    assert _persistent_expected(b, P)
+    kc_ref, vc_ref, slots_ref = oracle_caches(b, True)
+    ref = oracle.decode(b.q, kc_ref, vc_ref, b.block_tables, b.context_lens, b.scale, b.dtype,
+                        cache_dtype=b.cache_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
+    d = Device(b)
+    n = pa.decode_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size,
+                                 b.max_context_len, P)
+    ws = _random_workspace(n, 31)
+    fp8 = b.cache_dtype == "fp8"
+    say(f"append schedules {name} lens={lens} P={P}")
+    outs = []
+    for _ in range(3):
+        slots = torch.full((b.num_seqs,), 12345, dtype=torch.int32, device="cuda")
+        if fp8:
+            out = pa.decode_append_fp8(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens,
+                                       float(b.scale), float(b.k_scale), float(b.v_scale),
+                                       b.max_context_len, slot_mapping=slots, partition_size=P,
+                                       workspace=ws)
+        else:
+            out = pa.decode_append(d.q, d.k_new, d.v_new, d.kc, d.vc, d.bt, d.lens,
+                                   float(b.scale), b.max_context_len, 0, slot_mapping=slots,
+                                   partition_size=P, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), slots_ref)
+        assert _counter(ws) == 0 and _done_count(ws) == 0
+        outs.append(out)
+    down = (lambda t: t.cpu().numpy()) if fp8 else (
+        lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(down(d.kc), kc_ref) and np.array_equal(down(d.vc), vc_ref)
+    assert _same(outs[0], outs[1]) and _same(outs[1], outs[2])
+    err = max_err(outs[0], ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[b.dtype]

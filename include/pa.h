@@ -17,7 +17,9 @@
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; tensors are
  *    contiguous, row-major. The library allocates nothing, keeps no pointer
- *    after returning, and never synchronises the device.
+ *    after returning, and never synchronises the device. (Its one piece of
+ *    device memory is the fixed scratch array of pa_decode_append_static,
+ *    part of the loaded code object.)
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it asynchronously.
  *  - The arguments are validated on the host first; a negative status means
@@ -383,6 +385,38 @@ PA_API int pa_decode_append_fp8(const void* q, const void* k, const void* v, voi
                                 int32_t max_blocks_per_seq, int32_t max_context_len,
                                 int32_t partition_size, int32_t dtype, void* workspace,
                                 size_t workspace_size, void* stream);
+
+/*
+ * pa_decode_append_static -- pa_decode_append with no workspace argument:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results, preconditions and errors as pa_decode_append,
+ * without workspace / workspace_size: the split-K partials and the
+ * scheduler words live in a fixed array of PA_STATIC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU, held from the library's first use on
+ * that GPU until the process ends. The call allocates nothing (no hipMalloc,
+ * no allocating library routine); its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress) with the device current.
+ * Nothing in the array needs to start at zero: the partials of a call are
+ * written before they are read, and the scheduler words are read the way
+ * pa_decode reads a fresh workspace's.
+ * A call whose partials need more than PA_STATIC_SCRATCH_BYTES (as
+ * pa_decode_cascade_workspace_size counts them for the partition size the
+ * call uses) returns PA_ERR_WORKSPACE with nothing enqueued. Every call on
+ * one GPU shares that GPU's array: calls that can run at the same time on
+ * one GPU (other streams, other threads) race and give undefined results;
+ * serialize them, or use pa_decode_append with distinct workspaces.
+ */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20)
+PA_API int pa_decode_append_static(const void* q, const void* k, const void* v, void* key_cache,
+                                   void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, void* out,
+                                   int32_t* slot_mapping, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                   int64_t num_blocks, int32_t max_blocks_per_seq,
+                                   int32_t max_context_len, int32_t shared_prefix_blocks,
+                                   int32_t partition_size, int32_t dtype, void* stream);
 
 /*
  * Prefill batches ("01. PagedAttention 详解" §4, prefill phase: a prompt's N

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -34,6 +35,34 @@ int device_cu_count() {
     return 0;
   if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Workspace of pa_decode_append_static: one array per GPU, held by the loaded
+// code object until the process ends. Host code never passes its name to a
+// kernel (on the host the name is only a stand-in); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device (with it current) and kept.
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return PA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PA_OK;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -406,7 +435,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_DTYPE: return "unknown dtype code";
     case PA_ERR_UNSUPPORTED: return "no kernel for this head size, block size, group size, "
                                     "partition size or pointer alignment";
-    case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PA_ERR_WORKSPACE: return "split-K workspace missing or too small (pa_decode_append_static: "
+                                  "the call needs more than PA_STATIC_SCRATCH_BYTES)";
     case PA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case PA_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
     case PA_ERR_STATE: return "the block is not allocated in the pool (or freed more often than "
@@ -551,6 +581,30 @@ int pa_decode_append(const void* q, const void* k, const void* v, void* key_cach
                       num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
                       max_blocks_per_seq, max_context_len, shared_prefix_blocks, partition_size,
                       dtype, workspace, workspace_size, stream, ap);
+}
+
+int pa_decode_append_static(const void* q, const void* k, const void* v, void* key_cache,
+                            void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, float scale, void* out,
+                            int32_t* slot_mapping, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                            int64_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, int32_t shared_prefix_blocks,
+                            int32_t partition_size, int32_t dtype, void* stream) {
+  if (num_seqs > 0 && (!k || !v)) return PA_ERR_NULL;
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    const int st = static_scratch(&ws);
+    if (st != PA_OK) return st;
+  }
+  Append ap;
+  ap.k = k;
+  ap.v = v;
+  ap.slots = slot_mapping;
+  return cascade_impl(q, key_cache, value_cache, block_tables, context_lens, scale, out,
+                      num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+                      max_blocks_per_seq, max_context_len, shared_prefix_blocks, partition_size,
+                      dtype, ws, PA_STATIC_SCRATCH_BYTES, stream, ap);
 }
 
 int pa_decode_append_fp8(const void* q, const void* k, const void* v, void* key_cache,

@@ -62,6 +62,9 @@ SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _i32,
                                         _i32, _vp, _sz, _vp]),
+    "pa_decode_append_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp,
+                                               _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
+                                               _i32, _i32, _i32, _i32, _vp]),
     "pa_decode_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32,
                                             _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
                                             _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -306,6 +309,37 @@ def decode_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_cache: 
                                  int(partition_size), dtype_code(q.dtype), ws_ptr, ws_len,
                                  _stream(stream))
     _check("pa_decode_append", st)
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20   # PA_STATIC_SCRATCH_BYTES of include/pa.h
+
+
+def decode_append_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         max_context_len: int, shared_prefix_blocks: int = 0,
+                         out: Optional[torch.Tensor] = None,
+                         slot_mapping: Optional[torch.Tensor] = None, partition_size: int = 0,
+                         stream=None) -> torch.Tensor:
+    """decode_append with its split-K workspace in the library's fixed device array
+    (no allocation by the library; ``out`` is allocated here only when not given)."""
+    B, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    slots_ptr = _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None
+    st = load().pa_decode_append_static(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                        _dev(key_cache, "key_cache"),
+                                        _dev(value_cache, "value_cache"),
+                                        _dev(block_tables, "block_tables"),
+                                        _dev(context_lens, "context_lens"), float(scale),
+                                        _dev(out, "out"), slots_ptr, B, Hq, Hkv, D, bs, NB, MB,
+                                        int(max_context_len), int(shared_prefix_blocks),
+                                        int(partition_size), dtype_code(q.dtype),
+                                        _stream(stream))
+    _check("pa_decode_append_static", st)
     return out
 
 

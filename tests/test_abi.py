@@ -35,7 +35,8 @@ def test_header_declares_expected_api():
                                   "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count",
                                   "pa_pool_allocate", "pa_pool_free", "pa_pool_share",
                                   "pa_pool_copy_on_write", "pa_copy_blocks",
-                                  "pa_decode_append", "pa_decode_append_fp8"])
+                                  "pa_decode_append", "pa_decode_append_fp8",
+                                  "pa_decode_append_static"])
 
 
 def test_every_declared_symbol_is_exported_and_bound(lib):

@@ -179,27 +179,3 @@ def test_append_without_slot_output_and_workspace_reuse():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_mha", "gqa_8b", "prefix_shared_write",
-                                  "llama2_7b_mha_fp8"])
-def test_append_full_size_matches_separate_calls(name):
-    """At full size, in the launch configuration the benchmark times: slots and
-    pools against the oracle, every output row against the separate calls
-    (whose own oracle parity the decode tests cover), and a sample of output
-    rows against the oracle."""
-    spec = wl.CONFIGS[name]
-    b = wl.make_batch(spec)
-    pb = spec.shared_prefix_blocks
-    say(f"append full {name} B={b.num_seqs}")
-    _check(b, 0, prefix_blocks=pb, oracle_out=False)
-    d = Device(b)
-    _, out = _fused(b, d, 0, prefix_blocks=pb)
-    kc, vc, _ = oracle_caches(b, True)
-    rng = np.random.default_rng(7)
-    seqs = sorted(rng.choice(b.num_seqs, size=4, replace=False).tolist())
-    ref = oracle.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype,
-                        seqs=seqs, cache_dtype=b.cache_dtype, k_scale=b.k_scale,
-                        v_scale=b.v_scale)
-    got = out[seqs].float().cpu().numpy().astype(np.float64)
-    err = float(np.max(np.abs(got - ref)))
-    say(f"  sampled max abs err {err:.3e}")
-    assert err <= TOL[b.dtype]

@@ -78,33 +78,6 @@ def test_cascade_and_decode_scale_sign_zero_and_large(mult):
         assert err_p <= TOL[b.dtype]
 
 
-def test_cascade_prefix_workload_full_size_sampled():
-    """The full prefix-shared batch (128 sequences, 1024-token prefix, write
-    first) in the benchmark's launch configuration; sampled rows one by one,
-    plus agreement with the plain decode on every row."""
-    spec = wl.CONFIGS["prefix_shared_write"]
-    b = wl.make_batch(spec)
-    say(f"cascade full B={b.num_seqs} NB={b.num_blocks} maxlen={b.max_context_len}")
-    d = Device(b)
-    _write(b, d)
-    out = _cascade(b, d, 0)
-    plain = pa.decode(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale), b.max_context_len)
-    torch.cuda.synchronize()
-    assert float((out.float() - plain.float()).abs().max()) <= 2 * TOL[b.dtype]
-    kc, vc, _ = oracle_caches(b, True)
-    outf = out.float().cpu().numpy()
-    rng = np.random.default_rng(5)
-    pairs = {(0, 0), (b.num_seqs - 1, spec.num_q_heads - 1)}
-    while len(pairs) < 8:
-        pairs.add((int(rng.integers(b.num_seqs)), int(rng.integers(spec.num_q_heads))))
-    worst = 0.0
-    for s, h in sorted(pairs):
-        ref = oracle.decode_one(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype, s, h)
-        worst = max(worst, float(np.max(np.abs(outf[s, h] - ref))))
-    say(f"  worst sampled abs err {worst:.3e}")
-    assert worst <= TOL[b.dtype]
-
-
 def _edge_batch(bs, D, G, dtype, prefix_blocks, seed):
     Hkv = 2
     spec = wl.WorkloadSpec(name="cascade_edge", num_seqs=9, num_q_heads=Hkv * G,

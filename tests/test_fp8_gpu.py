@@ -88,31 +88,6 @@ def test_fp8_decode_small_all_outputs(name, P):
     assert err <= TOL[b.dtype]
 
 
-@pytest.mark.parametrize("name", wl.FP8_ORDER)
-def test_fp8_decode_full_size_sampled(name):
-    """Full-size batch in the benchmark's launch configuration (automatic
-    variant, quantizing write first); sampled rows recomputed one by one."""
-    spec = wl.CONFIGS[name]
-    b = wl.make_batch(spec)
-    say(f"fp8 decode full {name} B={b.num_seqs} NB={b.num_blocks} maxlen={b.max_context_len}")
-    d = Device(b)
-    _, out = gpu_step(b, d, write=True, partition_size=0)
-    kc, vc, _ = oracle_caches(b, True)
-    outf = out.float().cpu().numpy()
-    assert np.all(np.isfinite(outf))
-    rng = np.random.default_rng(99)
-    pairs = {(int(np.argmax(b.context_lens)), 0),
-             (int(np.argmin(b.context_lens)), spec.num_q_heads - 1)}
-    while len(pairs) < 8:
-        pairs.add((int(rng.integers(b.num_seqs)), int(rng.integers(spec.num_q_heads))))
-    worst = 0.0
-    for s, h in sorted(pairs):
-        ref = oracle_decode_one(b, kc, vc, s, h)
-        worst = max(worst, float(np.max(np.abs(outf[s, h].astype(np.float64) - ref))))
-    say(f"  worst sampled abs err {worst:.3e}")
-    assert worst <= TOL[b.dtype]
-
-
 EDGE_LENS = [1, 2, 15, 16, 17, 33, 512, 513, 1025, 0]
 
 

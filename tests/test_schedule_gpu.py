@@ -137,39 +137,6 @@ def test_workspace_shared_by_calls_of_different_shapes():
         assert max_err(first[key], ref) <= TOL[b.dtype]
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_mha", "gqa_8b", "long_context_splitk",
-                                  "llama2_7b_mha_fp8"])
-def test_workspace_reuse_full_size_sampled(name):
-    """Full-size batch with the automatic split and one workspace reused as the
-    benchmark reuses it: the counter-scheduled calls equal the first call
-    bitwise, and sampled outputs match the oracle."""
-    spec = wl.CONFIGS[name]
-    b = wl.make_batch(spec)
-    d = Device(b)
-    n = pa.decode_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size, b.max_context_len, 0)
-    ws = _random_workspace(n, 3)
-    head = ws[:4].clone()
-    say(f"schedule reuse full {name} B={b.num_seqs} maxlen={b.max_context_len}")
-    outs = [_decode(b, d, ws, 0) for _ in range(3)]
-    assert _head_rewritten(ws, head) == _persistent_expected(b, 0)
-    if _persistent_expected(b, 0):
-        assert _counter(ws) == 0
-    assert _same(outs[0], outs[1]) and _same(outs[1], outs[2])
-    kc, vc, _ = oracle_caches(b, False)
-    outf = outs[2].float().cpu().numpy()
-    assert np.all(np.isfinite(outf))
-    rng = np.random.default_rng(99)
-    worst = 0.0
-    picks = {(int(np.argmax(b.context_lens)), spec.num_q_heads - 1)}
-    while len(picks) < 5:
-        picks.add((int(rng.integers(b.num_seqs)), int(rng.integers(spec.num_q_heads))))
-    for s, h in sorted(picks):
-        ref = oracle_decode_one(b, kc, vc, s, h)
-        worst = max(worst, float(np.max(np.abs(outf[s, h].astype(np.float64) - ref))))
-    say(f"  worst sampled abs err {worst:.3e}")
-    assert worst <= TOL[b.dtype]
-
-
 def test_cascade_workspace_reuse():
     """Suffixes of up to 2500 tokens in 1024-token partitions: the cascade's
     suffix kernel runs on the persistent grid and its combine resets the

@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library ``libpa_gfx950.so`` in-tree with hipcc.
+"""Build the gfx950 HIP library ``libpa_gfx950.so`` in-tree with hipcc, and
+the benchmark's read-probe library ``libpa_probe_gfx950.so`` beside it.
 
 Usage: ``python -m paged_kv_cache_331_amd.build`` (or ``__graft_entry__.build()``).
 Every call recompiles. Objects go to ``_build/`` next to this file; the
@@ -22,6 +23,9 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ("pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_cascade.hip", "pa_prefill.hip",
            "pa_pool.cpp")
 ARCH = "gfx950"
+# Read-bandwidth probes used by bench.py only: a library of their own.
+PROBE_SOURCE = os.path.join(CSRC, "probe", "pa_probe.hip")
+PROBE_LIB_PATH = os.path.join(PKG, "libpa_probe_gfx950.so")
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -71,11 +75,14 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    probe_obj = os.path.join(BUILD_DIR, "pa_probe.o")
+    cmds.append([cc, *COMMON_FLAGS, "-c", PROBE_SOURCE, "-o", probe_obj])
     with ThreadPoolExecutor(min(len(cmds), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+    for path, inputs in ((LIB_PATH, objs), (PROBE_LIB_PATH, [probe_obj])):
+        tmp = path + f".tmp{os.getpid()}"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *inputs], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

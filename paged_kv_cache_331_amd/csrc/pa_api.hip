@@ -417,6 +417,8 @@ int cascade_impl(const void* q, const void* key_cache, const void* value_cache,
   a.prefix_row_tiles = (int32_t)((rows + rows_per_wg - 1) / rows_per_wg);
   set_sched(a, workspace, cus, false, group);
   set_append(a, ap, 1.f, 1.f);
+  const int64_t fold_bytes = (int64_t)group * c.chunks * (head_size + 2) * (int64_t)sizeof(float);
+  a.fold_lds_bytes = fold_bytes <= pa::kFoldLdsMaxBytes ? (int32_t)fold_bytes : 0;
   const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -67,6 +67,64 @@ __device__ __forceinline__ void fold_prefix(const DecodeParams& a, int64_t oh, i
   M = Mn;
 }
 
+// The same fold from a copy of the partials in LDS, laid out by
+// prefetch_prefix_partials: o [G][nslots][D], then m [G][nslots], then
+// l [G][nslots]; h is the head's index within the work-group's group.
+template <int G>
+__device__ __forceinline__ void fold_prefix_lds(const float* lds, int h, int d, int D, int nslots,
+                                                float& M, float& num, float& den) {
+  const float* po = lds + (h * nslots) * D + d;
+  const float* pm = lds + G * nslots * D + h * nslots;
+  const float* pl = pm + G * nslots;
+  float Mn = M;
+  for (int c = 0; c < nslots; ++c) Mn = fmaxf(Mn, pm[c]);
+  const float r = fast_exp2(M - Mn);
+  num *= r;
+  den *= r;
+  for (int c = 0; c < nslots; ++c) {
+    const float w = fast_exp2(pm[c] - Mn);
+    num = fmaf(w, po[c * D], num);
+    den = fmaf(w, pl[c], den);
+  }
+  M = Mn;
+}
+
+// Global memory -> LDS without registers (global_load_lds): each active lane
+// moves 16 (4) bytes from its own src to lds_wave + 16 (4) * lane, where
+// lds_wave is the same for the whole wave.
+__device__ __forceinline__ void lds_fetch16(const float* src, float* lds_wave) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_wave, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_fetch4(const float* src, float* lds_wave) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_wave, 4, 0, 0);
+}
+
+// Starts copying the prefix partials of the G query heads oh0 .. oh0+G-1
+// (slots 0 .. nslots-1 of each row) into LDS, in fold_prefix_lds's layout.
+// Nothing waits here: the copies land while the item's tiles stream, and the
+// wait for all outstanding loads before the cross-wave merge covers them.
+template <int D, int G>
+__device__ __forceinline__ void prefetch_prefix_partials(const DecodeParams& a, int64_t oh0,
+                                                         int nslots, float* lds, int tid) {
+  constexpr int NT = kDecodeWaves * 64;
+  const int lane = tid & 63;
+  const int per_head = nslots * D;                 // a multiple of 4 floats
+  for (int e = tid * 4; e < G * per_head; e += NT * 4) {
+    const int h = e / per_head;
+    const float* src = a.ws_o + (oh0 + h) * a.part_stride * D + (e - h * per_head);
+    lds_fetch16(src, lds + (e - lane * 4));
+  }
+  float* lm = lds + G * per_head;
+  for (int e = tid; e < G * nslots; e += NT) {
+    const int h = e / nslots;
+    const int64_t row = (oh0 + h) * a.part_stride + (e - h * nslots);
+    lds_fetch4(a.ws_m + row, lm + (e - lane));
+    lds_fetch4(a.ws_l + row, lm + G * nslots + (e - lane));
+  }
+}
+
 // Write-then-attend: the new token of sequence s (position app = L - 1) is
 // stored at its slot table[app / bs] * bs + app % bs, kv head g's part by
 // the first LPR threads (one token row of lanes, DL dimensions each); the
@@ -105,7 +163,12 @@ constexpr float kSlack = 8.f;              // lazy softmax reference: weights st
 constexpr int kTileTokens = 16;
 constexpr int kShortTileTokens = 8;
 constexpr int kShortPartition = 512;
+#ifndef PA_LONG_ITEM_TOKENS
+#define PA_LONG_ITEM_TOKENS 256
+#endif
+constexpr int kLongItemTokens = PA_LONG_ITEM_TOKENS;
 constexpr int kTableChunk = 256;           // table entries staged per LDS pass
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 
 union Vec16 {
   uint4 v;
@@ -125,7 +188,7 @@ struct DecodeLds {
 // TILE: tokens per wave iteration (raised to two load rows if smaller).
 template <class DT, class KT, int D, int G, bool APP, int TILE>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
-                                            DecodeLds<D, G>& sm) {
+                                            DecodeLds<D, G>& sm, float* fold_lds) {
   using S = Storage<DT>;
   constexpr int DL = LaneDims<KT, D>::value;   // dimensions held per lane (16 bytes)
   using KV = Kv<DT, KT, DL>;
@@ -178,6 +241,15 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   // in this launch, so no ordering between the store and the loads is needed.
   const bool own_app = APP && app >= start && app < end;
   const int end_main = own_app ? app : end;
+  // partitions holding tokens; one of them: this item writes the output
+  const int np = (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens;
+  const bool finish = np == 1 && !a.always_combine;
+  // A cascade item that finishes its sequence folds in the prefix partials:
+  // their loads start now, into LDS, and are waited for before the merge.
+  const bool fold_lds_ok = finish && a.slot_base > 0 && fold_lds != nullptr;
+  if (fold_lds_ok)
+    prefetch_prefix_partials<D, G>(a, (int64_t)s * a.num_q_heads + (int64_t)g * G, a.slot_base,
+                                   fold_lds, tid);
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -427,12 +499,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
       s_part[wave][h][D + 1] = Lh[h];
     }
   }
+  // The prefetched prefix partials have landed in LDS once this wave's loads
+  // are all done; the barrier extends that to every wave's share.
+  if (fold_lds_ok) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   // Merge the waves: rescale each wave's partial sums to the common max.
-  // partitions holding tokens
-  const int np = (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens;
-  const bool finish = np == 1 && !a.always_combine;
   for (int i = tid; i < G * D; i += NT) {
     const int h = i / D;
     const int d = i % D;
@@ -449,7 +521,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
     num *= a.v_scale;                                   // 1 unless the cache is FP8
     const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
     if (finish) {
-      if (a.slot_base > 0) fold_prefix(a, oh, d, D, a.slot_base, M, num, den);
+      if (fold_lds_ok)
+        fold_prefix_lds<G>(fold_lds, h, d, D, a.slot_base, M, num, den);
+      else if (a.slot_base > 0)
+        fold_prefix(a, oh, d, D, a.slot_base, M, num, den);
       a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
     } else {
       const int64_t pi = oh * a.part_stride + a.slot_base + p;
@@ -472,12 +547,28 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 template <class DT, class KT, int D, int G, bool APP, int TILE>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
+  extern __shared__ float fold_dyn[];          // a.fold_lds_bytes (cascade prefix partials)
   int wg = blockIdx.x;
   const int g = wg % a.num_kv_heads;
   wg /= a.num_kv_heads;
   const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
   const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
-  decode_item<DT, KT, D, G, APP, TILE>(a, g, s, p, sm);
+  float* const fold_lds = a.fold_lds_bytes > 0 ? fold_dyn : nullptr;
+  if constexpr (TILE < kTileTokens) {
+    // Short tiles, but an item of more than kLongItemTokens positions takes
+    // full tiles: twice the bytes in flight per wave and half the dependent
+    // rounds (512-token partitions of the long-context batch: 191 against
+    // 196 us). Not in a cascade, whose short suffix items all run at once
+    // and measured 1.5-2 us slower with it at thresholds of 128 to 256.
+    int L = a.lens[s];
+    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+    const int start = a.tok_offset + p * a.part_tokens;
+    if (a.slot_base == 0 && min(L, start + a.part_tokens) - start > kLongItemTokens) {
+      decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm, fold_lds);
+      return;
+    }
+  }
+  decode_item<DT, KT, D, G, APP, TILE>(a, g, s, p, sm, fold_lds);
 }
 
 // Persistent grid: gridDim.x (at most the item count) work-groups walk the
@@ -498,6 +589,8 @@ template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
   __shared__ int s_item[2];
+  extern __shared__ float fold_dyn[];          // a.fold_lds_bytes (cascade prefix partials)
+  float* const fold_lds = a.fold_lds_bytes > 0 ? fold_dyn : nullptr;
   const int Hkv = a.num_kv_heads;
   const int total = Hkv * a.num_seqs * a.num_parts;
   const uint32_t grid = gridDim.x;                 // <= total (host)
@@ -508,7 +601,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int g = it % Hkv;
     const int s = (it / Hkv) % a.num_seqs;
     const int p = it / (Hkv * a.num_seqs);
-    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
+    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm, fold_lds);
     if (!counted) {
       // The next item writes its waves' sums into sm.part, which threads of
       // this item may still be reading in the cross-wave merge: an item whose
@@ -711,7 +804,7 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   if (a.sched != nullptr && combine && a.persist_grid > 0) {
     const uint32_t grid = (uint32_t)(nwg < (uint64_t)a.persist_grid ? nwg : a.persist_grid);
     hipLaunchKernelGGL((decode_persistent_kernel<DT, KT, D, G, APP>), dim3(grid),
-                       dim3(kDecodeWaves * 64), 0, st, a);
+                       dim3(kDecodeWaves * 64), a.fold_lds_bytes, st, a);
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
@@ -721,10 +814,10 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
     if (short_tiles) {
       if constexpr (D == 128 && std::is_same<KT, DT>::value)
         hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kShortTileTokens>),
-                           dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
+                           dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), b.fold_lds_bytes, st, b);
     } else {
       hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kTileTokens>),
-                         dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
+                         dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), b.fold_lds_bytes, st, b);
     }
     if (!combine) return hipGetLastError();
     const hipError_t e = hipGetLastError();

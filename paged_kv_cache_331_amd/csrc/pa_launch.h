@@ -42,6 +42,10 @@ struct DecodeParams {
   int32_t prefix_chunks;    // prefix key chunks = partial slots 0 .. prefix_chunks-1
   int32_t prefix_row_tiles; // 64-row tiles of the num_seqs * group query rows
   int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
+  // Dynamic LDS of the partition kernels: room for the G query heads'
+  // prefix partials (G * prefix_chunks * (D + 2) floats), fetched at the
+  // start of a cascade item that folds them in; 0 = fold from global memory.
+  int32_t fold_lds_bytes = 0;
   // Persistent scheduling (split calls whose combine kernel runs): the
   // partition kernel is launched with persist_grid work-groups that take the
   // (kv head, sequence, partition) items from the scheduler word *sched: low
@@ -79,6 +83,9 @@ constexpr int kSchedDoneOffset = 128;
 // unit that takes the items from a counter. Launch shapes are fixed per
 // instantiation.
 constexpr int kDecodeWaves = 4;
+// Largest fold_lds_bytes a cascade call asks for (more prefix chunks fold
+// from global memory).
+constexpr int kFoldLdsMaxBytes = 24 * 1024;
 constexpr int kReduceThreads = 256;
 
 // Everything one prefill launch needs. Pointers are device pointers.

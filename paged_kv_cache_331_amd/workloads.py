@@ -417,6 +417,34 @@ def small_variant(name: str, num_seqs: int) -> WorkloadSpec:
     return replace(CONFIGS[name], num_seqs=num_seqs)
 
 
+def relabel_contiguous(batch: Batch) -> Batch:
+    """The same batch with its physical blocks renumbered so that every table
+    row is a run of consecutive ids in sequence order: shared prefix blocks
+    first, then each sequence's own blocks in table order (the contiguous
+    layout a non-paged cache would have). Pool rows move with their ids, so
+    every position keeps its K/V values and the attention result is the same;
+    only the physical placement changes. Unused blocks keep the ids after the
+    used ones; table entries past a sequence's blocks point at the pad block's
+    new id."""
+    bs = batch.spec.block_size
+    NB = batch.key_cache.shape[0]
+    order = []                       # old ids in their new order
+    seen = np.zeros(NB, dtype=bool)
+    for s in range(batch.num_seqs):
+        n = -(-int(batch.context_lens[s]) // bs)
+        for blk in batch.block_tables[s, :n].tolist():
+            if not seen[blk]:
+                seen[blk] = True
+                order.append(blk)
+    order.extend(np.flatnonzero(~seen).tolist())
+    order = np.asarray(order, dtype=np.int64)
+    new_id = np.empty(NB, dtype=np.int64)
+    new_id[order] = np.arange(NB)
+    return replace(batch, key_cache=batch.key_cache[order], value_cache=batch.value_cache[order],
+                   block_tables=new_id[batch.block_tables].astype(np.int32),
+                   used_blocks=new_id[batch.used_blocks], pad_block=int(new_id[batch.pad_block]))
+
+
 def poison_unused_blocks(batch: Batch) -> None:
     """Fill every physical block no table uses (including the pad block) with NaN."""
     mask = np.ones(batch.num_blocks, dtype=bool)

@@ -46,3 +46,15 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_oracle_timing_forks_workers_and_counts_items():
+    """The CPU baseline's process pool: every worker takes its own items and
+    the reported rate is items over the slowest worker's time."""
+    seen = []
+    rate, done, dt = bench.run_oracle_timed(lambda i: seen.append(i), 5, 0.05, 2)
+    assert done > 0 and dt >= 0.05 and abs(rate - done / dt) < 1e-9
+    assert seen == []          # the items ran in the forked workers, not here
+    rate1, done1, dt1 = bench.run_oracle_timed(lambda i: seen.append(i), 5, 0.02, 1)
+    assert done1 == len(seen) and seen[:5] == [0, 1, 2, 3, 4]
+    assert 1 <= bench.cpu_workers() <= 16

@@ -118,3 +118,34 @@ def test_fp8_pools_are_scaled_normal_codes(name):
         assert not np.any((pool & 0x7F) == 0x7F)
         x = oracle.e4m3_decode(pool[:64]) * float(b.k_scale)
         assert abs(x.mean()) < 0.02 and abs(x.std() - 1) < 0.03
+
+
+@pytest.mark.parametrize("name", ["tiny_write", "prefix_shared_write", "gqa_8b"])
+def test_relabel_contiguous_keeps_values_and_makes_runs(name):
+    """The contiguous renumbering used by the benchmark's layout comparison:
+    every table row becomes a run of consecutive block ids (the shared prefix
+    once, first), each position keeps its K/V row, and the oracle's output is
+    unchanged bit for bit."""
+    spec = wl.small_variant(name, min(wl.CONFIGS[name].num_seqs, 6))
+    b = wl.make_batch(spec)
+    c = wl.relabel_contiguous(b)
+    bs = spec.block_size
+    pfx = spec.shared_prefix_blocks
+    nxt = pfx
+    for s in range(b.num_seqs):
+        n = -(-int(b.context_lens[s]) // bs)
+        row = c.block_tables[s, :n]
+        if pfx:
+            assert np.array_equal(row[:pfx], np.arange(pfx))
+        assert np.array_equal(row[pfx:], np.arange(nxt, nxt + n - pfx))
+        nxt += n - pfx
+        for t in range(int(b.context_lens[s])):
+            a = int(b.block_tables[s, t // bs]), t % bs
+            z = int(c.block_tables[s, t // bs]), t % bs
+            assert np.array_equal(b.key_cache[a], c.key_cache[z])
+            assert np.array_equal(b.value_cache[a], c.value_cache[z])
+    ref = oracle.decode(b.q, b.key_cache, b.value_cache, b.block_tables, b.context_lens, b.scale,
+                        b.dtype)
+    got = oracle.decode(c.q, c.key_cache, c.value_cache, c.block_tables, c.context_lens, c.scale,
+                        c.dtype)
+    assert np.array_equal(ref, got)

@@ -170,6 +170,74 @@ constexpr int kLongItemTokens = PA_LONG_ITEM_TOKENS;
 constexpr int kTableChunk = 256;           // table entries staged per LDS pass
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 
+// Exchanges within a token row of 8 or 16 lanes, for reductions where lane c
+// pairs with a partner that differs in bit B of c: row_mirror (c <-> 15 - c)
+// for bit 3, row_half_mirror (c <-> 7 - c) for bit 2, quad xors for bits 1
+// and 0. The mirrors also flip the lower bits, which only reorders lanes
+// that hold the same values at that step of the reductions below.
+template <int B>
+__device__ __forceinline__ float partner(float x) {
+  if constexpr (B == 3) return dpp<kDppMirror>(x);
+  else if constexpr (B == 2) return dpp<kDppHalfMirror>(x);
+  else if constexpr (B == 1) return dpp<kDppQuadXor2>(x);
+  else return dpp<kDppQuadXor1>(x);
+}
+
+// One reduce-scatter step on bit B over the first N values: the lane keeps
+// the half its bit B selects, summed with the partner's copy of that half.
+template <int B, int N>
+__device__ __forceinline__ void scatter_step(float* v, int col) {
+  const bool hi = ((col >> B) & 1) != 0;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float keep = hi ? v[k + N / 2] : v[k];
+    const float send = hi ? v[k] : v[k + N / 2];
+    v[k] = keep + partner<B>(send);
+  }
+}
+
+// Reduce-scatter of N partial sums over the 2^LB lanes of a token row: lane
+// c ends with the complete sums of values c * N / 2^LB .. (c + 1) * N / 2^LB - 1
+// in v[0 ..], where each lane started with its share of every value.
+template <int N, int LB>
+__device__ __forceinline__ void reduce_scatter(float* v, int col) {
+  if constexpr (LB == 4) {
+    scatter_step<3, N>(v, col);
+    scatter_step<2, N / 2>(v, col);
+    scatter_step<1, N / 4>(v, col);
+    scatter_step<0, N / 8>(v, col);
+  } else {
+    scatter_step<2, N>(v, col);
+    scatter_step<1, N / 2>(v, col);
+    scatter_step<0, N / 4>(v, col);
+  }
+}
+
+// One all-gather step on bit B: the lane's N words and the partner's N words
+// (the neighbouring block) become 2N words in block order.
+template <int B, int N>
+__device__ __forceinline__ void gather_step(uint32_t* w, int col) {
+  const bool hi = ((col >> B) & 1) != 0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const uint32_t mine = w[k];
+    const uint32_t r = __float_as_uint(partner<B>(__uint_as_float(mine)));
+    w[k] = hi ? r : mine;
+    w[k + N] = hi ? mine : r;
+  }
+}
+
+// All-gather over bits B0 .. LB-1 of the lane index: each lane starts with the
+// W0 words of block c >> B0 (lanes that differ only in bits below B0 hold the
+// same block) and ends with all W0 << (LB - B0) words in block order.
+template <int W0, int B0, int LB>
+__device__ __forceinline__ void all_gather(uint32_t* w, int col) {
+  if constexpr (B0 <= 0) gather_step<0, W0>(w, col);
+  if constexpr (B0 <= 1) gather_step<1, (W0 << (1 - (B0 < 1 ? B0 : 1)))>(w, col);
+  if constexpr (B0 <= 2) gather_step<2, (W0 << (2 - (B0 < 2 ? B0 : 2)))>(w, col);
+  if constexpr (LB == 4 && B0 <= 3) gather_step<3, (W0 << (3 - (B0 < 3 ? B0 : 3)))>(w, col);
+}
+
 union Vec16 {
   uint4 v;
   uint32_t w[4];
@@ -292,9 +360,106 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   const int end_blk = end_main > start ? ((end_main - 1) >> lbs) + 1 : first_blk;
   const float sl2 = a.scale_log2;
 
+  // With at least as many (head, token) logits per tile as lanes in a token
+  // row (G * TG >= LPR: grouped heads), the partial dot products are
+  // reduce-scattered over the row instead of summed in every lane, so each
+  // lane completes J of them, all of one head (hc), and takes their
+  // exponentials alone; the packed weights are then gathered back to every
+  // lane of the row for p.V. Each lane keeps the running max of its head and
+  // a partial exp-sum, merged over the row at the end of the item.
+  constexpr int NL = G * TG;
+  constexpr bool kScatter = NL >= LPR;
+  constexpr int J = kScatter ? NL / LPR : 1;     // logits a lane completes
+  constexpr int SH = TG / J;                     // lanes per head in a token row
+  constexpr int LB = LPR == 16 ? 4 : 3;          // bits of the lane index within a row
+  static_assert(!kScatter || (J <= TG && TG % J == 0 && SH <= 4), "scatter layout");
+  float mh = kEmptyMax, lh = 0.f;
+
   // Online-softmax update of every token row with one 16-token tile whose K/V
   // rows are in kr / vr; positions >= tend are masked out.
   auto attend = [&](const int ts, const int tend, row_t (&kr)[TG], row_t (&vr)[TG]) {
+    if constexpr (kScatter) {
+      float v[NL];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) v[h * TG + tg] = KV::dot(qw[h], kr[tg], 0.f);
+      reduce_scatter<NL, LB>(v, col);
+      float lg[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) lg[j] = v[j] * sl2;
+      if (ts + kTile > tend) {                 // tail tile: mask positions >= tend
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          lg[j] = ts + ((col * J + j) % TG) * ROWS + row < tend ? lg[j] : -INFINITY;
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg)
+          vr[tg] = ts + tg * ROWS + row < tend ? vr[tg] : KV::zero();
+      }
+      uint32_t vw[TG][DL / 2];
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) KV::pairs(vr[tg], vw[tg]);
+
+      float mx = lg[0];
+#pragma unroll
+      for (int j = 1; j < J; ++j) mx = fmaxf(mx, lg[j]);
+      if constexpr (SH >= 2) mx = fmaxf(mx, dpp<kDppQuadXor1>(mx));
+      if constexpr (SH >= 4) mx = fmaxf(mx, dpp<kDppQuadXor2>(mx));
+      const bool up = mx > mh + kSlack;
+      const float mn = up ? mx : mh;
+      const float alpha = up ? fast_exp2(mh - mn) : 1.f;
+      mh = mn;
+      float pj[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) pj[j] = fast_exp2(lg[j] - mn);
+      if (__ballot(up) != 0) {                 // uniform: some head moved its reference
+        lh *= alpha;
+        const int row0 = lane & ~(LPR - 1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ah = __shfl(alpha, row0 + h * SH);
+#pragma unroll
+          for (int d = 0; d < DL; ++d) acc[h][d] *= ah;
+        }
+      }
+      // Weights rounded to QT in token pairs (tokens 2i, 2i+1 of a head), and
+      // the exp-sum of those rounded weights, counted once per pair.
+      uint32_t pw[NL / 2];
+      if constexpr (J >= 2) {
+#pragma unroll
+        for (int k = 0; k < J / 2; ++k) {
+          pw[k] = S::pack2(pj[2 * k], pj[2 * k + 1]);
+          lh = S::dot2(pw[k], S::kOnes, lh);
+        }
+        all_gather<J / 2, 0, LB>(pw, col);
+      } else {
+        const float pn = dpp<kDppQuadXor1>(pj[0]);   // the pair's other token
+        const bool odd = (col & 1) != 0;
+        pw[0] = odd ? S::pack2(pn, pj[0]) : S::pack2(pj[0], pn);
+        const float lt = S::dot2(pw[0], S::kOnes, lh);
+        lh = odd ? lh : lt;
+        all_gather<1, 1, LB>(pw, col);
+      }
+#pragma unroll
+      for (int i = 0; i < TG / 2; ++i) {
+        uint32_t vlo[DL / 2], vhi[DL / 2];
+#pragma unroll
+        for (int e = 0; e < DL / 2; ++e) {
+          vlo[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x05040100u);
+          vhi[e] = __builtin_amdgcn_perm(vw[2 * i + 1][e], vw[2 * i][e], 0x07060302u);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint32_t pp = pw[h * (TG / 2) + i];
+#pragma unroll
+          for (int e = 0; e < DL / 2; ++e) {
+            acc[h][2 * e] = S::dot2(pp, vlo[e], acc[h][2 * e]);
+            acc[h][2 * e + 1] = S::dot2(pp, vhi[e], acc[h][2 * e + 1]);
+          }
+        }
+      }
+      return;
+    }
     float lg[G][TG];
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -441,6 +606,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   // of the values, adding the partner's copy of that half, and leaves the
   // other half to the partner, so lane (row, col) ends with the totals of
   // values row * n .. row * n + n - 1 (value h * DL + d), n = G * DL / R.
+  if constexpr (kScatter) {
+    // Per-head state of the token row, as the unreduced path keeps it: the
+    // max from the first lane of each head, the exp-sum over its lanes.
+    float lsum = lh;
+    if constexpr (SH >= 2) lsum += dpp<kDppQuadXor1>(lsum);
+    if constexpr (SH >= 4) lsum += dpp<kDppQuadXor2>(lsum);
+    const int row0 = lane & ~(LPR - 1);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = __shfl(mh, row0 + h * SH);
+      l[h] = __shfl(lsum, row0 + h * SH);
+    }
+  }
   static_assert(LPR == 8 || LPR == 16, "row lanes");
   constexpr int N = G * DL;
   constexpr int n = LPR == 8 ? N / 8 : N / 4;

@@ -42,8 +42,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ("paged_kv_cache_331_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_331_amd/csrc/pa_device.h",
                   "paged_kv_cache_331_amd/csrc/pa_launch.h",
-                  "paged_kv_cache_331_amd/csrc/pa_cascade.hip",
                   "paged_kv_cache_331_amd/csrc/pa_mq.h",
+                  "paged_kv_cache_331_amd/csrc/pa_prefix.h",
                   "paged_kv_cache_331_amd/csrc/pa_api.hip")
 
 
@@ -115,8 +115,9 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
     ``copy_bytes`` (the calibration run, ``--copy-probe``): the copy fetches
     and writes exactly ``copy_bytes``. A decode call is the partition kernel
     (one work-group per item, or the persistent grid) plus, when split, the
-    reduce kernel, and in a cascade the shared-prefix kernel before them; the
-    median over dispatches of each is summed. The record is keyed to the kernel sources' hash so that it
+    reduce kernel; a cascade is its one launch of suffix items and prefix
+    work-groups plus the reduce kernel. The median over dispatches of each is
+    summed. The record is keyed to the kernel sources' hash so that it
     stops being reported once the kernels change.
     """
     def median_kib(path, counter, match):
@@ -133,7 +134,7 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
     rec = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_fetch,
            "write_scale": f_write, "kernels": {}}
     total = 0.0
-    for tag in ("cascade_prefix_kernel", "decode_partition_kernel", "decode_persistent_kernel",
+    for tag in ("cascade_fused_kernel", "decode_partition_kernel", "decode_persistent_kernel",
                 "decode_reduce_kernel", "decode_reduce_few_kernel"):
         m = lambda k, tag=tag: tag in k
         try:

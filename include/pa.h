@@ -300,8 +300,9 @@ PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_h
  *     a kv head against one read of the prefix's K/V, as dense matrix
  *     products on the matrix cores (keys at or past a sequence's own length
  *     are masked, so a sequence shorter than the prefix is still exact);
- *   - each sequence's positions [prefix_len, L) on the ordinary partition
- *     kernel (partition_size as in pa_decode, applied to that range);
+ *   - each sequence's positions [prefix_len, L) as the ordinary decode items
+ *     (partition_size as in pa_decode, applied to that range), one
+ *     work-group per item, in the same launch as the prefix part;
  *   - the combine of both kinds of partials, as in the split path.
  * The softmax weights enter the matrix products rounded to the query's 2-byte
  * type; accumulation stays fp32. The prefix is read through row 0 of
@@ -310,7 +311,9 @@ PA_API size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_q_h
  * is range-checked).
  * shared_prefix_blocks : 0 .. max_blocks_per_seq (0 = a plain pa_decode call)
  * workspace            : at least pa_decode_cascade_workspace_size(...) bytes,
- *                        256-byte aligned; used as pa_decode uses its workspace
+ *                        256-byte aligned; contents need no initialisation, and
+ *                        its first 256 bytes (pa_decode's scheduler words) are
+ *                        left as they are
  * Errors: those of pa_decode, and PA_ERR_SHAPE for shared_prefix_blocks out
  * of range or (with shared_prefix_blocks > 0 and num_seqs > 0) num_blocks
  * == 0 or num_blocks * block_size above INT32_MAX (slots are int32). Caches

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libpa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ("pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_cascade.hip", "pa_prefill.hip",
+SOURCES = ("pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_prefill.hip",
            "pa_pool.cpp")
 ARCH = "gfx950"
 # Read-bandwidth probes used by bench.py only: a library of their own.

@@ -410,15 +410,13 @@ int cascade_impl(const void* q, const void* key_cache, const void* value_cache,
   a.tok_offset = c.prefix_len;
   a.slot_base = c.chunks;
   a.part_stride = c.slots;
-  a.always_combine = 0;     // one-partition suffixes fold the prefix in the partition kernel
+  a.always_combine = 1;     // prefix and suffix partials meet in the combine kernel
   a.prefix_len = c.prefix_len;
   a.prefix_chunks = c.chunks;
   const int rows_per_wg = pa::cascade_rows_per_wg(head_size);
   a.prefix_row_tiles = (int32_t)((rows + rows_per_wg - 1) / rows_per_wg);
-  set_sched(a, workspace, cus, false, group);
+  clear_sched(a);           // one work-group per item: the scheduler words stay as they are
   set_append(a, ap, 1.f, 1.f);
-  const int64_t fold_bytes = (int64_t)group * c.chunks * (head_size + 2) * (int64_t)sizeof(float);
-  a.fold_lds_bytes = fold_bytes <= pa::kFoldLdsMaxBytes ? (int32_t)fold_bytes : 0;
   const hipError_t e = pa::launch_cascade(a, dtype, head_size, group, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

@@ -42,88 +42,10 @@
 
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_prefix.h"
 
 namespace pa {
 namespace {
-
-// Folds the shared-prefix partials (slots 0 .. nslots-1 of row oh, written by
-// the cascade's prefix kernel) into a running (M, num, den) of one output
-// element d: the split-K rescale by 2^(m - M).
-__device__ __forceinline__ void fold_prefix(const DecodeParams& a, int64_t oh, int d, int D,
-                                            int nslots, float& M, float& num, float& den) {
-  const float* pm = a.ws_m + oh * a.part_stride;
-  const float* pl = a.ws_l + oh * a.part_stride;
-  const float* po = a.ws_o + oh * a.part_stride * D + d;
-  float Mn = M;
-  for (int c = 0; c < nslots; ++c) Mn = fmaxf(Mn, pm[c]);
-  const float r = fast_exp2(M - Mn);
-  num *= r;
-  den *= r;
-  for (int c = 0; c < nslots; ++c) {
-    const float w = fast_exp2(pm[c] - Mn);
-    num = fmaf(w, po[(int64_t)c * D], num);
-    den = fmaf(w, pl[c], den);
-  }
-  M = Mn;
-}
-
-// The same fold from a copy of the partials in LDS, laid out by
-// prefetch_prefix_partials: o [G][nslots][D], then m [G][nslots], then
-// l [G][nslots]; h is the head's index within the work-group's group.
-template <int G>
-__device__ __forceinline__ void fold_prefix_lds(const float* lds, int h, int d, int D, int nslots,
-                                                float& M, float& num, float& den) {
-  const float* po = lds + (h * nslots) * D + d;
-  const float* pm = lds + G * nslots * D + h * nslots;
-  const float* pl = pm + G * nslots;
-  float Mn = M;
-  for (int c = 0; c < nslots; ++c) Mn = fmaxf(Mn, pm[c]);
-  const float r = fast_exp2(M - Mn);
-  num *= r;
-  den *= r;
-  for (int c = 0; c < nslots; ++c) {
-    const float w = fast_exp2(pm[c] - Mn);
-    num = fmaf(w, po[c * D], num);
-    den = fmaf(w, pl[c], den);
-  }
-  M = Mn;
-}
-
-// Global memory -> LDS without registers (global_load_lds): each active lane
-// moves 16 (4) bytes from its own src to lds_wave + 16 (4) * lane, where
-// lds_wave is the same for the whole wave.
-__device__ __forceinline__ void lds_fetch16(const float* src, float* lds_wave) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)lds_wave, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_fetch4(const float* src, float* lds_wave) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)lds_wave, 4, 0, 0);
-}
-
-// Starts copying the prefix partials of the G query heads oh0 .. oh0+G-1
-// (slots 0 .. nslots-1 of each row) into LDS, in fold_prefix_lds's layout.
-// Nothing waits here: the copies land while the item's tiles stream, and the
-// wait for all outstanding loads before the cross-wave merge covers them.
-template <int D, int G>
-__device__ __forceinline__ void prefetch_prefix_partials(const DecodeParams& a, int64_t oh0,
-                                                         int nslots, float* lds, int tid) {
-  constexpr int NT = kDecodeWaves * 64;
-  const int lane = tid & 63;
-  const int per_head = nslots * D;                 // a multiple of 4 floats
-  for (int e = tid * 4; e < G * per_head; e += NT * 4) {
-    const int h = e / per_head;
-    const float* src = a.ws_o + (oh0 + h) * a.part_stride * D + (e - h * per_head);
-    lds_fetch16(src, lds + (e - lane * 4));
-  }
-  float* lm = lds + G * per_head;
-  for (int e = tid; e < G * nslots; e += NT) {
-    const int h = e / nslots;
-    const int64_t row = (oh0 + h) * a.part_stride + (e - h * nslots);
-    lds_fetch4(a.ws_m + row, lm + (e - lane));
-    lds_fetch4(a.ws_l + row, lm + G * nslots + (e - lane));
-  }
-}
 
 // Write-then-attend: the new token of sequence s (position app = L - 1) is
 // stored at its slot table[app / bs] * bs + app % bs, kv head g's part by
@@ -168,7 +90,6 @@ constexpr int kShortPartition = 512;
 #endif
 constexpr int kLongItemTokens = PA_LONG_ITEM_TOKENS;
 constexpr int kTableChunk = 256;           // table entries staged per LDS pass
-constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 
 // Exchanges within a token row of 8 or 16 lanes, for reductions where lane c
 // pairs with a partner that differs in bit B of c: row_mirror (c <-> 15 - c)
@@ -256,7 +177,7 @@ struct DecodeLds {
 // TILE: tokens per wave iteration (raised to two load rows if smaller).
 template <class DT, class KT, int D, int G, bool APP, int TILE>
 __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s, int p,
-                                            DecodeLds<D, G>& sm, float* fold_lds) {
+                                            DecodeLds<D, G>& sm) {
   using S = Storage<DT>;
   constexpr int DL = LaneDims<KT, D>::value;   // dimensions held per lane (16 bytes)
   using KV = Kv<DT, KT, DL>;
@@ -284,21 +205,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   if (start >= L) {
     // The first partition of a sequence with no token past the offset stores
     // its appended token (inside a cascade's shared prefix, which callers
-    // must not do: the prefix kernel has already read that block).
+    // must not do: the prefix work-groups of the same launch read that block).
     if (APP && p == 0) append_row<KV, DL, LPR>(a, s, g, app, D, tid);
+    // An empty sequence's output is zero (a cascade's combine writes it).
     if (p == 0 && !a.always_combine) {
-      // No token past the offset: an empty sequence stays zero; in a cascade a
-      // sequence that ends inside the shared prefix is the prefix partials alone.
       uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
-      const bool pfx = a.slot_base > 0 && L > 0;
-      for (int i = tid; i < G * D; i += NT) {
-        float M = kEmptyMax, num = 0.f, den = 0.f;
-        if (pfx) {
-          const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + i / D;
-          fold_prefix(a, oh, i % D, D, a.slot_base, M, num, den);
-        }
-        o[i] = pfx ? S::from_float(num / den) : (uint16_t)0;
-      }
+      for (int i = tid; i < G * D; i += NT) o[i] = 0;
     }
     return;
   }
@@ -312,12 +224,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   // partitions holding tokens; one of them: this item writes the output
   const int np = (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens;
   const bool finish = np == 1 && !a.always_combine;
-  // A cascade item that finishes its sequence folds in the prefix partials:
-  // their loads start now, into LDS, and are waited for before the merge.
-  const bool fold_lds_ok = finish && a.slot_base > 0 && fold_lds != nullptr;
-  if (fold_lds_ok)
-    prefetch_prefix_partials<D, G>(a, (int64_t)s * a.num_q_heads + (int64_t)g * G, a.slot_base,
-                                   fold_lds, tid);
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -677,9 +583,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
       s_part[wave][h][D + 1] = Lh[h];
     }
   }
-  // The prefetched prefix partials have landed in LDS once this wave's loads
-  // are all done; the barrier extends that to every wave's share.
-  if (fold_lds_ok) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   // Merge the waves: rescale each wave's partial sums to the common max.
@@ -699,10 +602,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
     num *= a.v_scale;                                   // 1 unless the cache is FP8
     const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
     if (finish) {
-      if (fold_lds_ok)
-        fold_prefix_lds<G>(fold_lds, h, d, D, a.slot_base, M, num, den);
-      else if (a.slot_base > 0)
-        fold_prefix(a, oh, d, D, a.slot_base, M, num, den);
       a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
     } else {
       const int64_t pi = oh * a.part_stride + a.slot_base + p;
@@ -725,28 +624,25 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 template <class DT, class KT, int D, int G, bool APP, int TILE>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
-  extern __shared__ float fold_dyn[];          // a.fold_lds_bytes (cascade prefix partials)
   int wg = blockIdx.x;
   const int g = wg % a.num_kv_heads;
   wg /= a.num_kv_heads;
   const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
   const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
-  float* const fold_lds = a.fold_lds_bytes > 0 ? fold_dyn : nullptr;
   if constexpr (TILE < kTileTokens) {
     // Short tiles, but an item of more than kLongItemTokens positions takes
     // full tiles: twice the bytes in flight per wave and half the dependent
     // rounds (512-token partitions of the long-context batch: 191 against
-    // 196 us). Not in a cascade, whose short suffix items all run at once
-    // and measured 1.5-2 us slower with it at thresholds of 128 to 256.
+    // 196 us).
     int L = a.lens[s];
     L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
     const int start = a.tok_offset + p * a.part_tokens;
-    if (a.slot_base == 0 && min(L, start + a.part_tokens) - start > kLongItemTokens) {
-      decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm, fold_lds);
+    if (min(L, start + a.part_tokens) - start > kLongItemTokens) {
+      decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
       return;
     }
   }
-  decode_item<DT, KT, D, G, APP, TILE>(a, g, s, p, sm, fold_lds);
+  decode_item<DT, KT, D, G, APP, TILE>(a, g, s, p, sm);
 }
 
 // Persistent grid: gridDim.x (at most the item count) work-groups walk the
@@ -767,8 +663,6 @@ template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
   __shared__ DecodeLds<D, G> sm;
   __shared__ int s_item[2];
-  extern __shared__ float fold_dyn[];          // a.fold_lds_bytes (cascade prefix partials)
-  float* const fold_lds = a.fold_lds_bytes > 0 ? fold_dyn : nullptr;
   const int Hkv = a.num_kv_heads;
   const int total = Hkv * a.num_seqs * a.num_parts;
   const uint32_t grid = gridDim.x;                 // <= total (host)
@@ -779,7 +673,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int g = it % Hkv;
     const int s = (it / Hkv) % a.num_seqs;
     const int p = it / (Hkv * a.num_seqs);
-    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm, fold_lds);
+    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
     if (!counted) {
       // The next item writes its waves' sums into sm.part, which threads of
       // this item may still be reading in the cross-wave merge: an item whose
@@ -958,6 +852,36 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_few_kernel(const
   *o = packed;
 }
 
+// Cascade decode in one launch. Work-groups [0, items) are the suffix items
+// (kv head fastest, then sequence, then partition), the rest the prefix
+// work-groups of pa_prefix.h. Every item writes partials, which the combine
+// kernel that follows merges with the prefix partials, so no work-group
+// waits on another: the prefix work-groups take the slots that the shortest
+// suffix items leave, and run while the longest ones still read. The launch
+// holds the larger of the two LDS footprints; the prefix work-groups keep
+// kFusedPrefixRing steps of loads in flight so that the suffix items keep
+// four work-groups per CU (two at G = 8, whose items need the registers).
+template <int G> struct FusedWavesPerEu { static constexpr int value = G <= 4 ? 4 : 2; };
+template <class DT, int D, int G, bool APP, int TILE>
+__global__ __launch_bounds__(kDecodeWaves * 64, FusedWavesPerEu<G>::value) void cascade_fused_kernel(
+    const DecodeParams a) {
+  static_assert(cascade_waves(D) == kDecodeWaves, "one work-group shape for both kinds");
+  __shared__ union {
+    DecodeLds<D, G> dec;
+    PrefixLds<D, kFusedPrefixRing> pre;
+  } sm;
+  const int Hkv = a.num_kv_heads;
+  const int items = Hkv * a.num_seqs * a.num_parts;
+  int wg = blockIdx.x;
+  if (wg >= items) {
+    cascade_prefix_wg<DT, D, G, kFusedPrefixRing, true>(a, wg - items, sm.pre);
+    return;
+  }
+  const int g = wg % Hkv;
+  wg /= Hkv;
+  decode_item<DT, DT, D, G, APP, TILE>(a, g, wg % a.num_seqs, wg / a.num_seqs, sm.dec);
+}
+
 template <class DT, int D>
 hipError_t launch_combine(const DecodeParams& a, hipStream_t st) {
   if (a.slot_base + a.num_parts <= kFewParts) {
@@ -982,7 +906,7 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   if (a.sched != nullptr && combine && a.persist_grid > 0) {
     const uint32_t grid = (uint32_t)(nwg < (uint64_t)a.persist_grid ? nwg : a.persist_grid);
     hipLaunchKernelGGL((decode_persistent_kernel<DT, KT, D, G, APP>), dim3(grid),
-                       dim3(kDecodeWaves * 64), a.fold_lds_bytes, st, a);
+                       dim3(kDecodeWaves * 64), 0, st, a);
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
@@ -992,10 +916,10 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
     if (short_tiles) {
       if constexpr (D == 128 && std::is_same<KT, DT>::value)
         hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kShortTileTokens>),
-                           dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), b.fold_lds_bytes, st, b);
+                           dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
     } else {
       hipLaunchKernelGGL((decode_partition_kernel<DT, KT, D, G, APP, kTileTokens>),
-                         dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), b.fold_lds_bytes, st, b);
+                         dim3((uint32_t)nwg), dim3(kDecodeWaves * 64), 0, st, b);
     }
     if (!combine) return hipGetLastError();
     const hipError_t e = hipGetLastError();
@@ -1033,7 +957,62 @@ hipError_t launch_t(const DecodeParams& a, int head_size, int group, hipStream_t
   }
 }
 
+template <class DT, int D, int G, bool APP>
+hipError_t launch_fused(const DecodeParams& a, hipStream_t st) {
+  const uint64_t items = (uint64_t)a.num_kv_heads * a.num_parts * a.num_seqs;
+  const uint64_t pre = (uint64_t)a.num_kv_heads * a.prefix_row_tiles * a.prefix_chunks;
+  if (items + pre == 0) return hipSuccess;
+  if (items + pre > 0x7fffffffull) return hipErrorInvalidConfiguration;
+  DecodeParams b = a;
+  b.sched = nullptr;                     // not a persistent launch: the words stay as they are
+  if constexpr (D == 128) {
+    if (a.part_tokens <= kShortPartition) {
+      hipLaunchKernelGGL((cascade_fused_kernel<DT, D, G, APP, kShortTileTokens>),
+                         dim3((uint32_t)(items + pre)), dim3(kDecodeWaves * 64), 0, st, b);
+      const hipError_t e = hipGetLastError();
+      return e != hipSuccess ? e : launch_combine<DT, D>(b, st);
+    }
+  }
+  hipLaunchKernelGGL((cascade_fused_kernel<DT, D, G, APP, kTileTokens>),
+                     dim3((uint32_t)(items + pre)), dim3(kDecodeWaves * 64), 0, st, b);
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : launch_combine<DT, D>(b, st);
+}
+
+template <class DT, int D, int G>
+hipError_t launch_fused_a(const DecodeParams& a, hipStream_t st) {
+  return a.k_new != nullptr ? launch_fused<DT, D, G, true>(a, st)
+                            : launch_fused<DT, D, G, false>(a, st);
+}
+
+template <class DT, int D>
+hipError_t launch_fused_g(const DecodeParams& a, int group, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_fused_a<DT, D, 1>(a, st);
+    case 2: return launch_fused_a<DT, D, 2>(a, st);
+    case 4: return launch_fused_a<DT, D, 4>(a, st);
+    case 8: return launch_fused_a<DT, D, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class DT>
+hipError_t launch_fused_d(const DecodeParams& a, int head_size, int group, hipStream_t st) {
+  switch (head_size) {
+    case 64: return launch_fused_g<DT, 64>(a, group, st);
+    case 128: return launch_fused_g<DT, 128>(a, group, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cascade(const DecodeParams& a, int dtype, int head_size, int group,
+                          hipStream_t stream) {
+  if (!a.always_combine) return hipErrorInvalidValue;
+  return dtype == 0 ? launch_fused_d<Fp16>(a, head_size, group, stream)
+                    : launch_fused_d<Bf16>(a, head_size, group, stream);
+}
 
 hipError_t launch_decode(const DecodeParams& a, int dtype, bool fp8_cache, int head_size,
                          int group, hipStream_t stream) {

@@ -42,10 +42,6 @@ struct DecodeParams {
   int32_t prefix_chunks;    // prefix key chunks = partial slots 0 .. prefix_chunks-1
   int32_t prefix_row_tiles; // 64-row tiles of the num_seqs * group query rows
   int32_t len_cap;          // lengths are clamped to this (max_context_len, table reach)
-  // Dynamic LDS of the partition kernels: room for the G query heads'
-  // prefix partials (G * prefix_chunks * (D + 2) floats), fetched at the
-  // start of a cascade item that folds them in; 0 = fold from global memory.
-  int32_t fold_lds_bytes = 0;
   // Persistent scheduling (split calls whose combine kernel runs): the
   // partition kernel is launched with persist_grid work-groups that take the
   // (kv head, sequence, partition) items from the scheduler word *sched: low
@@ -83,9 +79,6 @@ constexpr int kSchedDoneOffset = 128;
 // unit that takes the items from a counter. Launch shapes are fixed per
 // instantiation.
 constexpr int kDecodeWaves = 4;
-// Largest fold_lds_bytes a cascade call asks for (more prefix chunks fold
-// from global memory).
-constexpr int kFoldLdsMaxBytes = 24 * 1024;
 constexpr int kReduceThreads = 256;
 
 // Everything one prefill launch needs. Pointers are device pointers.
@@ -128,13 +121,21 @@ constexpr int cascade_rows_per_wg(int head_size) {
   return cascade_waves(head_size) * 16 * kCascadeRowBlocks;
 }
 
+// Steps of K/V loads in flight in the prefix work-groups of the cascade
+// launch (their LDS ring sets the launch's LDS footprint).
+#ifndef PA_FUSED_PREFIX_RING
+#define PA_FUSED_PREFIX_RING 1
+#endif
+constexpr int kFusedPrefixRing = PA_FUSED_PREFIX_RING;
+
 // One decode step: the partition kernel, then (num_parts > 1) the combine.
 // dtype: q / out type (0 fp16, 1 bf16); fp8_cache: the caches hold E4M3 codes.
 hipError_t launch_decode(const DecodeParams& a, int dtype, bool fp8_cache, int head_size,
                          int group, hipStream_t stream);
 
-// Cascade decode: the prefix kernel (MFMA), the partition kernel over the
-// positions past the prefix, then the combine of both kinds of partials.
+// Cascade decode: one launch holding the suffix items (the positions past
+// the prefix) and the prefix work-groups (MFMA), every one writing partials,
+// then the combine of both kinds. a.always_combine must be 1.
 hipError_t launch_cascade(const DecodeParams& a, int dtype, int head_size, int group,
                           hipStream_t stream);
 

@@ -26,8 +26,9 @@
 //
 // Memory: each step's K and V tiles (32 keys x D, 2-byte) go from global
 // memory straight into LDS (global_load_lds_dwordx4, no registers), read
-// once per work-group, kMqRing steps ahead of their use, into a ring of
-// kMqRing + 1 LDS buffers. Both tiles are row-major and swizzled so that
+// once per work-group, RD steps ahead of their use (kMqRing by default; the
+// cascade's prefix work-groups take 1 to fit beside the decode items), into
+// a ring of RD + 1 LDS buffers. Both tiles are row-major and swizzled so that
 // their reads spread over the banks: in K the 16-byte chunk c of key row r
 // sits at chunk c ^ (r % 16) (A-operand reads, 16 rows per pass), in V the
 // 32-byte unit u at u ^ (r % 8) at head size 128 (transposed reads,
@@ -116,11 +117,11 @@ __device__ __forceinline__ float mq_sum_over_groups(float x) {
   return a + b;
 }
 
-// K and V tiles of kMqBufs steps, row-major (key, dimension), swizzled as
-// described above.
-template <int D> struct MqLds {
-  alignas(16) uint16_t k[kMqBufs][kMqStep][D];
-  alignas(16) uint16_t v[kMqBufs][kMqStep][D];
+// K and V tiles of NB steps (the ring of loads in flight plus the step
+// computed), row-major (key, dimension), swizzled as described above.
+template <int D, int NB = kMqBufs> struct MqLds {
+  alignas(16) uint16_t k[NB][kMqStep][D];
+  alignas(16) uint16_t v[NB][kMqStep][D];
 };
 
 // Source of the loads of positions that hold no key.
@@ -199,10 +200,14 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 // work-group may use). Must be reached by all threads of the work-group with
 // the same c0 / kend (it synchronises); LDS is free again when it returns.
 // sl2 (scale * log2 e) must be >= 0: mq_load_q folds a negative scale's sign
-// into q.
-template <class DT, int D, int RB, int W = kMqWaves, class SlotOf>
+// into q. RD: steps of loads in flight (the ring holds RD + 1 steps). LEAN:
+// read each V^T fragment just before its product instead of all of them
+// before the softmax (32 fewer VGPRs at head size 128, for callers that
+// share a register budget).
+template <class DT, int D, int RB, int W = kMqWaves, int RD = kMqRing, bool LEAN = false,
+          class SlotOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
-                                          MqLds<D>& lds, const uint16_t* kc, const uint16_t* vc,
+                                          MqLds<D, RD + 1>& lds, const uint16_t* kc, const uint16_t* vc,
                                           int64_t tok_stride, int g, int c0, int kend,
                                           const int (&row_end)[RB], float sl2, SlotOf slot_of) {
   constexpr int KS = D / 32;
@@ -212,8 +217,8 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   constexpr int TILE = kMqStep * D * 2;        // bytes of one K or V tile
   constexpr int SPW = TILE / 1024 / W;         // 1 KB tile slices each wave loads
   static_assert(SPW >= 1 && TILE % (1024 * W) == 0, "tile slices");
-  constexpr int RD = kMqRing;
-  constexpr int NB = kMqBufs;
+  constexpr int NB = RD + 1;
+  static_assert(RD >= 1, "at least one step in flight");
   constexpr int DPS = 2 * SPW;                 // LDS loads a wave issues per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,14 +311,18 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
         for (int b = 0; b < RB; ++b) c[b][kt] = Mma<DT>::run(kv, qb[b][ks], c[b][kt]);
       }
     }
-    // V^T fragments of every dimension tile, read before the softmax so the
-    // LDS latency hides behind it: keys 4g .. 4g+3, then 16+4g .. 16+4g+3.
-    u32x4_t va[DTILES];
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
+    // V^T fragment of dimension tile dt: keys 4g .. 4g+3, then 16+4g .. 16+4g+3.
+    auto read_va = [&](int dt) {
       const uint2 lo = mq_lds_read_tr16(va_addr[dt] + bo);
       const uint2 hi = mq_lds_read_tr16(va_addr[dt] + bo + 16 * D * 2);
-      va[dt] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    };
+    // Unless LEAN, every fragment is read before the softmax, so the LDS
+    // latency hides behind it.
+    u32x4_t va[LEAN ? 1 : DTILES];
+    if constexpr (!LEAN) {
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) va[dt] = read_va(dt);
     }
     u32x4_t pb[RB];
     float m_old[RB];
@@ -376,16 +385,21 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.lsum[b] = Storage<DT>::dot2(pb[b][e], Storage<DT>::kOnes, st.lsum[b]);
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt)
+    for (int dt = 0; dt < DTILES; ++dt) {
+      const u32x4_t v = LEAN ? read_va(dt) : va[LEAN ? 0 : dt];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) st.acc[b][dt] = Mma<DT>::run(va[dt], pb[b], st.acc[b][dt]);
+      for (int b = 0; b < RB; ++b) st.acc[b][dt] = Mma<DT>::run(v, pb[b], st.acc[b][dt]);
+    }
   };
 
   // Step i lives in LDS buffer i % NB. Steps i + 1 .. i + RD - 1 are in
-  // flight while step i computes; after it, step i + RD goes into the buffer
-  // of step i - 1, which every wave finished before the barrier of step i.
+  // flight while step i computes; step i + RD goes into the buffer of step
+  // i - 1, which every wave finished before the barrier of step i. With a
+  // single step in flight it is issued right after that barrier, so that its
+  // loads overlap step i's products; deeper rings issue it after them.
   // Steps past the range load zeros and are never computed, so the count of
   // loads in flight is the same at every step.
+  constexpr bool kIssueFirst = RD == 1;
   const int nsteps = kend > c0 ? (kend - c0 + kMqStep - 1) / kMqStep : 0;
 #pragma unroll
   for (int r = 0; r < RD; ++r) issue(c0 + r * kMqStep, r);
@@ -396,8 +410,9 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
       if (step >= nsteps) break;                  // uniform
       mq_wait_loads<(RD - 1) * DPS>();            // this wave's loads of this step
       __syncthreads();                            // everyone's
+      if (kIssueFirst) issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
       compute(c0 + step * kMqStep, r);
-      issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
+      if (!kIssueFirst) issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
     }
   }
   mq_wait_loads<0>();

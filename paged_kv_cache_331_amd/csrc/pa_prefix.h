@@ -1,4 +1,4 @@
-// Cascade decode for a shared prefix, gfx950.
+// Cascade decode for a shared prefix, gfx950: the prefix work-groups.
 //
 // When every sequence of the batch starts with the same physical blocks (a
 // prompt prefix held once with a reference count per user: "01.
@@ -7,41 +7,51 @@
 //   * the prefix part: the query rows of ALL sequences against the one copy
 //     of the prefix's K/V. For each kv head this is a dense product of
 //     (num_seqs * group) query rows with prefix_len keys, so it runs on the
-//     matrix cores and reads the prefix from HBM once instead of once per
-//     sequence;
-//   * the suffix part: each sequence's own positions past the prefix, on the
-//     ordinary partition kernel;
+//     matrix cores (the core of pa_mq.h) and reads the prefix from HBM once
+//     instead of once per sequence;
+//   * the suffix part: each sequence's own positions past the prefix, as the
+//     ordinary decode items;
 //   * the combine of both kinds of (max, exp-sum, weighted V) partials, with
 //     the split-K algebra of the ordinary path.
 // The result is the plain attention of every position < L (an exact
 // reformulation, up to fp32 rounding and the 2-byte rounding of the
-// softmax weights fed to the matrix cores).
+// softmax weights fed to the matrix cores). The first two parts share one
+// launch (cascade_fused_kernel in pa_decode.hip); the combine kernel follows.
 //
-// Prefix kernel layout: one work-group (cascade_waves(D) waves of
-// kCascadeRowBlocks 16-row blocks: 4 x 1 at both head sizes) per
-// (kv head, row tile, chunk of kPrefixChunk prefix keys), on the matrix-core
-// attention core of pa_mq.h. Rows are (sequence, query head) pairs of the kv
-// head; each row's keys end at min(L, prefix_len), and the work-group writes
-// a (max, exp-sum, unnormalised O) partial per row for its chunk.
+// This file holds the prefix part as a work-group body. Work-group wg of
+// (kv head g, row tile rt, chunk): wg = g + Hkv * (rt + row_tiles * chunk),
+// cascade_waves(D) waves of kCascadeRowBlocks 16-row blocks (4 x 1 at both
+// head sizes). Rows are (sequence, query head) pairs of kv head g; each row's
+// keys end at min(L, prefix_len); the work-group writes one (reference max,
+// exp-sum, unnormalised O) partial per row into partial slot `chunk` of the
+// workspace. RD: steps of K/V loads in flight (the LDS ring holds RD + 1);
+// LEAN: the core's lower-register form (see mq_attend).
+#pragma once
+
 #include "pa_device.h"
 #include "pa_launch.h"
 #include "pa_mq.h"
 
 namespace pa {
-namespace {
 
-template <class DT, int D, int G>
-__global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(const DecodeParams a) {
+template <int D, int RD>
+struct PrefixLds {
+  int32_t tbl[kPrefixChunk / 16];
+  int limit[cascade_waves(D)];
+  MqLds<D, RD + 1> mq;
+};
+
+template <class DT, int D, int G, int RD, bool LEAN = false>
+__device__ __forceinline__ void cascade_prefix_wg(const DecodeParams& a, int wg,
+                                                  PrefixLds<D, RD>& sm) {
   constexpr int W = cascade_waves(D);
   constexpr int RB = kCascadeRowBlocks;
   constexpr int NT = W * 64;
   static_assert(D == 64 || D == 128, "head size");
-  __shared__ int32_t s_tbl[kPrefixChunk / 16];
-  __shared__ int s_limit[W];
-  __shared__ MqLds<D> lds;
+  int32_t* s_tbl = sm.tbl;
+  int* s_limit = sm.limit;
 
   const int Hkv = a.num_kv_heads;
-  int wg = blockIdx.x;
   const int g = wg % Hkv;
   wg /= Hkv;
   const int rt = wg % a.prefix_row_tiles;
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(c
     const int blk = s_tbl[(t >> lbs) - b0];
     return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
   };
-  mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(a.kc),
+  mq_attend<DT, D, RB, W, RD, LEAN>(st, qb, sm.mq, static_cast<const uint16_t*>(a.kc),
                           static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend,
                           row_end, fabsf(a.scale_log2), slot_of);
 
@@ -130,46 +140,6 @@ __global__ __launch_bounds__(cascade_waves(D) * 64) void cascade_prefix_kernel(c
       *reinterpret_cast<float4*>(po + 16 * dt) =
           make_float4(st.acc[b][dt][0], st.acc[b][dt][1], st.acc[b][dt][2], st.acc[b][dt][3]);
   }
-}
-
-template <class DT, int D, int G>
-hipError_t launch_prefix(const DecodeParams& a, hipStream_t st) {
-  const uint64_t nwg = (uint64_t)a.num_kv_heads * a.prefix_row_tiles * a.prefix_chunks;
-  if (nwg == 0) return hipSuccess;
-  if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((cascade_prefix_kernel<DT, D, G>), dim3((uint32_t)nwg),
-                     dim3(cascade_waves(D) * 64), 0, st, a);
-  return hipGetLastError();
-}
-
-template <class DT, int D>
-hipError_t launch_prefix_g(const DecodeParams& a, int group, hipStream_t st) {
-  switch (group) {
-    case 1: return launch_prefix<DT, D, 1>(a, st);
-    case 2: return launch_prefix<DT, D, 2>(a, st);
-    case 4: return launch_prefix<DT, D, 4>(a, st);
-    case 8: return launch_prefix<DT, D, 8>(a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <class DT>
-hipError_t launch_prefix_d(const DecodeParams& a, int head_size, int group, hipStream_t st) {
-  switch (head_size) {
-    case 64: return launch_prefix_g<DT, 64>(a, group, st);
-    case 128: return launch_prefix_g<DT, 128>(a, group, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
-
-hipError_t launch_cascade(const DecodeParams& a, int dtype, int head_size, int group,
-                          hipStream_t stream) {
-  const hipError_t e = dtype == 0 ? launch_prefix_d<Fp16>(a, head_size, group, stream)
-                                  : launch_prefix_d<Bf16>(a, head_size, group, stream);
-  if (e != hipSuccess) return e;
-  return launch_decode(a, dtype, false, head_size, group, stream);
 }
 
 }  // namespace pa

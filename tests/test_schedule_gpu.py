@@ -28,6 +28,9 @@ def _lib():
     assert torch.cuda.is_available()
 
 
+SCHED_HEAD_BYTES = 256   # the workspace's leading scheduler words (include/pa.h)
+
+
 def _random_workspace(nbytes: int, seed: int) -> torch.Tensor:
     g = torch.Generator(device="cuda").manual_seed(seed)
     return torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
@@ -138,9 +141,10 @@ def test_workspace_shared_by_calls_of_different_shapes():
 
 
 def test_cascade_workspace_reuse():
-    """Suffixes of up to 2500 tokens in 1024-token partitions: the cascade's
-    suffix kernel runs on the persistent grid and its combine resets the
-    counter."""
+    """Suffixes of up to 2500 tokens in 1024-token partitions, one workspace of
+    random bytes reused: the one-launch cascade runs its suffix items one
+    work-group per item beside the prefix work-groups, so it leaves the
+    scheduler words as it found them, and every call gives the same output."""
     spec = dataclasses.replace(wl.CONFIGS["prefix_shared_write"], num_seqs=32, len_hi=2500)
     b = wl.make_batch(spec)
     d = Device(b)
@@ -149,14 +153,14 @@ def test_cascade_workspace_reuse():
     n = pa.decode_cascade_workspace_size(b.num_seqs, spec.num_q_heads, spec.head_size,
                                          spec.block_size, b.max_context_len, pfx, P)
     ws = _random_workspace(n, 11)
-    head = ws[:4].clone()
+    words = ws[:SCHED_HEAD_BYTES].clone()
     say(f"schedule reuse cascade B={b.num_seqs} prefix_blocks={pfx}")
     outs = []
     for _ in range(3):
         outs.append(pa.decode_cascade(d.q, d.kc, d.vc, d.bt, d.lens, float(b.scale),
                                       b.max_context_len, pfx, partition_size=P, workspace=ws))
         torch.cuda.synchronize()
-    assert _head_rewritten(ws, head) and _counter(ws) == 0
+    assert torch.equal(ws[:SCHED_HEAD_BYTES], words)
     assert _same(outs[0], outs[1]) and _same(outs[1], outs[2])
     ref = oracle.decode(b.q, b.key_cache, b.value_cache, b.block_tables, b.context_lens, b.scale,
                         b.dtype)

@@ -170,6 +170,46 @@ struct DecodeLds {
   float part[kDecodeWaves][G][D + 2];
 };
 
+// The end of an item: each wave has left its per-head (max, exp-sum) in
+// part[wave][h][D], part[wave][h][D + 1] and its unnormalised sums in
+// part[wave][h][0 .. D-1] (the caller synchronised). The waves are merged by
+// rescaling each to the common max; the item writes its output rows
+// (finish) or its partials in slot slot_base + p.
+template <class DT, int D, int G>
+__device__ __forceinline__ void merge_waves(const DecodeParams& a, int s, int g, int p,
+                                            bool finish, const float (&part)[kDecodeWaves][G][D + 2],
+                                            int tid) {
+  using S = Storage<DT>;
+  constexpr int NW = kDecodeWaves;
+  constexpr int NT = NW * 64;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = part[0][h][D];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, part[w][h][D]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = fast_exp2(part[w][h][D] - M);
+      num = fmaf(c, part[w][h][d], num);
+      den = fmaf(c, part[w][h][D + 1], den);
+    }
+    num *= a.v_scale;                                   // 1 unless the cache is FP8
+    const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
+    if (finish) {
+      a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
+    } else {
+      const int64_t pi = oh * a.part_stride + a.slot_base + p;
+      a.ws_o[pi * D + d] = num;
+      if (d == 0) {
+        a.ws_m[pi] = M;
+        a.ws_l[pi] = den;
+      }
+    }
+  }
+}
+
 // One work item: kv head g, sequence s, partition p. Uniform over the
 // work-group (every thread takes the same path and the same barriers).
 // APP: the call appends each sequence's new token (write-then-attend);
@@ -585,33 +625,322 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
   }
   __syncthreads();
 
-  // Merge the waves: rescale each wave's partial sums to the common max.
-  for (int i = tid; i < G * D; i += NT) {
-    const int h = i / D;
-    const int d = i % D;
-    float M = s_part[0][h][D];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_part[w][h][D]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float c = fast_exp2(s_part[w][h][D] - M);
-      num = fmaf(c, s_part[w][h][d], num);
-      den = fmaf(c, s_part[w][h][D + 1], den);
+  merge_waves<DT, D, G>(a, s, g, p, finish, s_part, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core decode item for an FP8 cache at head size 128 with G >= 4 query
+// heads per kv head. The VALU item above spends most of its issue slots on
+// the dot products of the G heads (two v_dot2 per code and head); here they
+// are matrix-core products with the G heads as G of the 16 columns:
+//   S^T (16 positions x 16 heads)  = K (16 x 128) . Q^T (128 x 16)     (v_mfma_f32_16x16x32)
+//   O^T (16 dims x 16 heads)      += V^T (16 x 16) . P^T (16 x 16)     (v_mfma_f32_16x16x16, per dimension tile)
+// A wave takes 16-position steps of the item in turn. Each step's K and V
+// rows (16 x 128 codes each) go from global memory straight into a per-wave
+// LDS ring (global_load_lds_dwordx4) kF8Ring steps ahead, so a wave only
+// waits on its own loads; the codes become the query's 2-byte type (exactly)
+// as the operands are read:
+//   * K as the A operand: lane l holds position l % 16 and codes
+//     32 ks + 8 (l / 16) .. + 7 of slice ks (ds_read_b64);
+//   * V^T as the A operand, via ds_read_b64_tr_b8: lane j of each 16-lane
+//     group gets byte j % 8 of the row addressed by group lane 2 y + j / 8 as
+//     its byte y. Group lane 2 y + h points at position 4 (l / 16) + y % 4,
+//     dimensions 16 (2 dd + y / 4) + 8 h, so lane j gets dimension 32 dd + j
+//     of its four positions in bytes 0-3 and dimension 32 dd + 16 + j in
+//     bytes 4-7: two dimension tiles per read.
+// The k order of P^T is the four positions 4 (l / 16) .. + 3 whose logits
+// the lane holds in S^T, so no weight crosses lanes. Rows of a tile are 128
+// bytes; the 16-byte unit u of row T sits at u ^ key(T), which keeps both
+// kinds of reads free of bank conflicts. Positions past the item's end, and
+// blocks whose table entry is out of range, load a zero chunk and are
+// masked; the online softmax is the lazy-reference one of the VALU item,
+// per column.
+#ifndef PA_F8_RING
+#define PA_F8_RING 2
+#endif
+constexpr int kF8Ring = PA_F8_RING;              // steps of loads in flight per wave
+constexpr int kF8Bufs = kF8Ring + 1;
+constexpr int kF8Step = 16;                      // positions per step
+constexpr int kF8Tile = kF8Step * 128;           // bytes of one step's K (or V) codes
+constexpr int kF8Loads = 2 * (kF8Tile / 1024);   // load instructions per step and wave
+
+struct F8Ring {
+  alignas(16) uint8_t k[kDecodeWaves][kF8Bufs][kF8Tile];
+  alignas(16) uint8_t v[kDecodeWaves][kF8Bufs][kF8Tile];
+};
+
+template <int G>
+struct F8Lds {
+  int32_t tbl[kTableChunk];
+  union {
+    F8Ring ring;                                 // during the walk
+    float part[kDecodeWaves][G][128 + 2];        // after it (behind a barrier)
+  };
+};
+
+// Bijective on the 8 rows of each parity (K reads: 16 consecutive rows at
+// one unit), and rows 4q and 4q + 2 (or 4q + 1 and 4q + 3) differ in bit 2
+// (V reads: units 2 dd and 2 dd + 1 of four consecutive rows).
+__device__ __forceinline__ int f8_key(int T) { return ((T & 2) << 1) | ((T >> 2) & 3); }
+
+typedef int f8_v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) f8_v2i f8_lds_v2i;
+typedef short f8_s4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f8_h4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 f8_lds_read8(uint32_t addr) {
+  const f8_v2i r = *reinterpret_cast<const f8_lds_v2i*>(mq_lds_ptr(addr));
+  return make_uint2((uint32_t)r.x, (uint32_t)r.y);
+}
+__device__ __forceinline__ uint2 f8_lds_read8_tr(uint32_t addr) {
+  const f8_v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<f8_lds_v2i*>(mq_lds_ptr(addr)));
+  return make_uint2((uint32_t)r.x, (uint32_t)r.y);
+}
+// Eight codes (two words) as a 16x16x32 operand of the query's 2-byte type.
+template <class QT>
+__device__ __forceinline__ u32x4_t f8_operand(uint2 w) {
+  return u32x4_t{Fp8Pair<QT>::template get<false>(w.x), Fp8Pair<QT>::template get<true>(w.x),
+                 Fp8Pair<QT>::template get<false>(w.y), Fp8Pair<QT>::template get<true>(w.y)};
+}
+// O^T += A . B with 16x16x16 operands (four values of the 2-byte type).
+template <class QT> struct Mma16;
+template <> struct Mma16<Fp16> {
+  static __device__ __forceinline__ f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f8_h4, a),
+                                                 __builtin_bit_cast(f8_h4, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma16<Bf16> {
+  static __device__ __forceinline__ f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(f8_s4, a),
+                                                     __builtin_bit_cast(f8_s4, b), c, 0, 0, 0);
+  }
+};
+
+template <class QT, int G, bool APP>
+__device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, int s, int p,
+                                                  F8Lds<G>& sm) {
+  using S = Storage<QT>;
+  using KV = Kv<QT, Fp8, 16>;
+  constexpr int D = 128;
+  constexpr int NW = kDecodeWaves;
+  constexpr int NT = NW * 64;
+  constexpr int RD = kF8Ring;
+  constexpr int NB = kF8Bufs;
+  static_assert(G >= 4 && G <= 16, "heads as matrix columns");
+  const int Hkv = a.num_kv_heads;
+  const int tid = threadIdx.x;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int start = a.tok_offset + p * a.part_tokens;
+  const int app = APP ? L - 1 : -1;
+  if (start >= L) {
+    if (APP && p == 0) append_row<KV, 16, 8>(a, s, g, app, D, tid);
+    if (p == 0 && !a.always_combine) {
+      uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
+      for (int i = tid; i < G * D; i += NT) o[i] = 0;
     }
-    num *= a.v_scale;                                   // 1 unless the cache is FP8
-    const int64_t oh = (int64_t)s * a.num_q_heads + (int64_t)g * G + h;
-    if (finish) {
-      a.out[oh * D + d] = S::from_float(den > 0.f ? num / den : 0.f);
-    } else {
-      const int64_t pi = oh * a.part_stride + a.slot_base + p;
-      a.ws_o[pi * D + d] = num;
-      if (d == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = den;
+    return;
+  }
+  const int end = min(L, start + a.part_tokens);
+  const bool own_app = APP && app >= start && app < end;
+  const int end_main = own_app ? app : end;
+  const int np = (L - a.tok_offset + a.part_tokens - 1) / a.part_tokens;
+  const bool finish = np == 1 && !a.always_combine;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 15;                     // head column / row of a 16-row operand
+  const int gq = lane >> 4;
+  const int64_t tok_stride = (int64_t)Hkv * D;   // bytes between slots
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kc) + (int64_t)g * D;
+  const uint8_t* vc = static_cast<const uint8_t*>(a.vc) + (int64_t)g * D;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(kMqZeroChunk);
+
+  // Q^T as the B operand: column j = head j of the group (zero past G),
+  // slice ks = dimensions 32 ks + 8 gq .. + 7.
+  u32x4_t qb[4];
+  {
+    const bool ok = j < G;
+    const uint16_t* qs = a.q + ((int64_t)s * a.num_q_heads + (int64_t)g * G + (ok ? j : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qb[ks] = ok ? *reinterpret_cast<const u32x4_t*>(qs + 32 * ks + 8 * gq) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // LDS byte offsets within a tile. K reads: row j, slice ks. V^T reads: row
+  // 4 gq + y % 4 with y = j / 2, units 2 dd + y / 4, half j & 1.
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    koff[ks] = j * 128 + (((2 * ks + (gq >> 1)) ^ f8_key(j)) << 4) + 8 * (gq & 1);
+  {
+    const int y = j >> 1;
+    const int T = 4 * gq + (y & 3);
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+      voff[dd] = T * 128 + (((2 * dd + (y >> 2)) ^ f8_key(T)) << 4) + 8 * (j & 1);
+  }
+  // Loads: wave-load w of a tile fills bytes [1024 w, +1024): this lane's 16
+  // bytes are unit lane % 8 of row 8 w + lane / 8, which holds source unit
+  // (lane % 8) ^ key(row).
+  uint32_t lsrc[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) lsrc[w] = (uint32_t)(((lane & 7) ^ f8_key(8 * w + (lane >> 3))) << 4);
+
+  const uint32_t kr0 = (uint32_t)(uintptr_t)&sm.ring.k[wave][0][0];
+  const uint32_t vr0 = (uint32_t)(uintptr_t)&sm.ring.v[wave][0][0];
+  const int32_t* bt_row = a.bt + (int64_t)s * a.max_blocks_per_seq;
+  const int bs = a.block_size;
+  const int lbs = a.log2_block_size;
+  const float sl2 = a.scale_log2;
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kEmptyMax, lsum = 0.f;
+
+  // Step k of this wave in the staged table chunk at block cb (positions
+  // t0 + 16 (wave + NW k) ..) into ring buffer k % NB. A step past the
+  // wave's last (k >= mine) loads the zero chunk, so every step issues the
+  // same number of loads. Returns whether the step's block entry is bad.
+  auto issue = [&](int t0, int cb, int tend, int k, int mine) -> bool {
+    const int ts = t0 + kF8Step * (wave + NW * k);
+    const int blk = k < mine ? __builtin_amdgcn_readfirstlane(sm.tbl[min((ts >> lbs) - cb, kTableChunk - 1)]) : -1;
+    const bool okb = (uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks;
+    const uint32_t buf = (uint32_t)(k % NB) * kF8Tile;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int t = ts + 8 * w + (lane >> 3);  // this lane's position
+      const bool ok = okb && t < tend;
+      const int64_t row = ((int64_t)blk * bs + (t & (bs - 1))) * tok_stride + lsrc[w];
+      mq_lds_load16_nt(ok ? kc + row : zero, kr0 + buf + (uint32_t)w * 1024);
+      mq_lds_load16_nt(ok ? vc + row : zero, vr0 + buf + (uint32_t)w * 1024);
+    }
+    return !okb;
+  };
+
+  // One step from ring buffer buf: positions ts .. ts + 15, masked at tend.
+  auto compute = [&](int ts, int tend, uint32_t buf, bool bad) {
+    const uint32_t kt = kr0 + buf;
+    const uint32_t vt = vr0 + buf;
+    f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      c = Mma<QT>::run(f8_operand<QT>(f8_lds_read8(kt + koff[ks])), qb[ks], c);
+    float lg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lg[i] = ts + 4 * gq + i < tend && !bad ? c[i] * sl2 : -INFINITY;
+    float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mx = mq_max_over_groups(mx);
+    const bool up = mx > m + kSlack;
+    const float mn = up ? mx : m;
+    if (__ballot(up) != 0) {                   // uniform: some head moved its reference
+      const float alpha = fast_exp2(m - mn);   // 1 where this column did not move
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    }
+    m = mn;
+    uint2 pb;
+    pb.x = Mma<QT>::pack(fast_exp2(lg[0] - mn), fast_exp2(lg[1] - mn));
+    pb.y = Mma<QT>::pack(fast_exp2(lg[2] - mn), fast_exp2(lg[3] - mn));
+    lsum = S::dot2(pb.x, S::kOnes, lsum);
+    lsum = S::dot2(pb.y, S::kOnes, lsum);
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      const u32x4_t v = f8_operand<QT>(f8_lds_read8_tr(vt + voff[dd]));
+      acc[2 * dd] = Mma16<QT>::run(make_uint2(v[0], v[1]), pb, acc[2 * dd]);
+      acc[2 * dd + 1] = Mma16<QT>::run(make_uint2(v[2], v[3]), pb, acc[2 * dd + 1]);
+    }
+  };
+
+  const int first_blk = start >> lbs;            // start is block aligned
+  const int end_blk = end_main > start ? ((end_main - 1) >> lbs) + 1 : first_blk;
+  for (int cb = first_blk; cb < end_blk; cb += kTableChunk) {
+    const int nb = min(kTableChunk, end_blk - cb);
+    if (cb != first_blk) __syncthreads();        // previous chunk fully consumed
+    for (int i = tid; i < nb; i += NT) sm.tbl[i] = bt_row[cb + i];
+    __syncthreads();
+    const int t0 = cb << lbs;
+    const int t1 = min(end_main, (cb + nb) << lbs);
+    const int nsteps = (t1 - t0 + kF8Step - 1) / kF8Step;
+    const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;   // uniform
+    if (mine == 0) continue;
+    bool bad[NB];
+#pragma unroll
+    for (int r = 0; r < RD; ++r) bad[r] = issue(t0, cb, t1, r, mine);
+    for (int k0 = 0; k0 < mine; k0 += NB) {
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int k = k0 + r;
+        if (k >= mine) break;                    // uniform
+        bad[(r + RD) % NB] = issue(t0, cb, t1, k + RD, mine);
+        mq_wait_loads<RD * kF8Loads>();          // step k's loads have landed
+        compute(t0 + kF8Step * (wave + NW * k), t1, (uint32_t)r * kF8Tile, bad[r]);
       }
     }
+    mq_wait_loads<0>();                          // the ring is free again
   }
+
+  // The new token, in the wave that would take the next step: a step whose
+  // row 0 holds its codes (quantized as the cache write does) and whose other
+  // rows are zero, masked past app. Lanes 0-7 also store it at the slot.
+  const int app_wave = ((end_main - start + kF8Step - 1) / kF8Step) % NW;
+  if (own_app && wave == app_wave) {             // uniform
+    const int32_t blk = __builtin_amdgcn_readfirstlane(bt_row[app >> lbs]);
+    const int32_t slot = blk * bs + (app & (bs - 1));
+    if (g == 0 && lane == 0 && a.slots_out) a.slots_out[s] = slot;
+    if ((uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks) {
+      // Every load of this wave has landed and been read: buffer 0 is free.
+      mq_lds_u32x4* kz = reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(kr0));
+      mq_lds_u32x4* vz = reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(vr0));
+#pragma unroll
+      for (int i = 0; i < kF8Tile / 16 / 64; ++i) {
+        kz[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
+        vz[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if (lane < 8) {
+        const int64_t src = ((int64_t)s * Hkv + g) * D + 16 * lane;
+        const typename KV::row kn = KV::from_src(a.k_new + src, a.k_scale_w);
+        const typename KV::row vn = KV::from_src(a.v_new + src, a.v_scale_w);
+        const int64_t dst = (int64_t)slot * tok_stride + 16 * lane;
+        KV::store(const_cast<uint8_t*>(kc) + dst, kn);
+        KV::store(const_cast<uint8_t*>(vc) + dst, vn);
+        kz[lane] = u32x4_t{kn[0], kn[1], kn[2], kn[3]};   // row 0: unit u at u ^ key(0) = u
+        vz[lane] = u32x4_t{vn[0], vn[1], vn[2], vn[3]};
+      }
+      compute(app, app + 1, 0, false);           // the wave's LDS accesses stay in order
+    }
+  }
+
+  // Merge: column j (head j < G) of this wave, its dimensions 16 dt + 4 gq + i.
+  const float lh = mq_sum_over_groups(lsum);
+  __syncthreads();                               // every wave is done with the ring
+  if (j < G) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.part[wave][j][16 * dt + 4 * gq + i] = acc[dt][i];
+    if (gq == 0) {
+      sm.part[wave][j][D] = m;
+      sm.part[wave][j][D + 1] = lh;
+    }
+  }
+  __syncthreads();
+  merge_waves<QT, D, G>(a, s, g, p, finish, sm.part, tid);
+}
+
+// One work-group per item, in the partition kernel's grid order.
+template <class QT, int G, bool APP>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_f8mma_kernel(const DecodeParams a) {
+  __shared__ F8Lds<G> sm;
+  int wg = blockIdx.x;
+  const int g = wg % a.num_kv_heads;
+  wg /= a.num_kv_heads;
+  const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
+  const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
+  decode_item_f8mma<QT, G, APP>(a, g, s, p, sm);
 }
 
 // One work-group per item. Work-groups are numbered kv head fastest. With
@@ -910,6 +1239,16 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
+    if constexpr (std::is_same<KT, Fp8>::value && D == 128 && G >= 4) {
+      // FP8 cache with grouped heads: the matrix-core item (non-temporal
+      // LDS loads, two steps in flight: 156 against 168 us for the VALU
+      // item on the FP8 GQA-8B batch).
+      hipLaunchKernelGGL((decode_f8mma_kernel<DT, G, APP>), dim3((uint32_t)nwg),
+                         dim3(kDecodeWaves * 64), 0, st, b);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || !combine) return e;
+      return launch_combine<DT, D>(b, st);
+    }
     bool short_tiles = false;
     if constexpr (D == 128 && std::is_same<KT, DT>::value)
       short_tiles = a.part_tokens <= kShortPartition;

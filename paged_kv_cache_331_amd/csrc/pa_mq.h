@@ -135,6 +135,10 @@ __device__ __forceinline__ void mq_lds_load16(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 // Until at most N of this wave's global loads are outstanding.
+// The same with the non-temporal hint, for rows read once per launch.
+__device__ __forceinline__ void mq_lds_load16_nt(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
+}
 template <int N> __device__ __forceinline__ void mq_wait_loads() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }

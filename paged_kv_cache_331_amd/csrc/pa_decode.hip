@@ -629,103 +629,165 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core decode item for an FP8 cache at head size 128 with G >= 4 query
-// heads per kv head. The VALU item above spends most of its issue slots on
-// the dot products of the G heads (two v_dot2 per code and head); here they
-// are matrix-core products with the G heads as G of the 16 columns:
+// Matrix-core decode item for head size 128 with G >= 4 query heads per kv
+// head. The VALU item above spends most of its issue slots on the dot
+// products of the G heads; here they are matrix-core products with the G
+// heads as G of the 16 columns:
 //   S^T (16 positions x 16 heads)  = K (16 x 128) . Q^T (128 x 16)     (v_mfma_f32_16x16x32)
 //   O^T (16 dims x 16 heads)      += V^T (16 x 16) . P^T (16 x 16)     (v_mfma_f32_16x16x16, per dimension tile)
 // A wave takes 16-position steps of the item in turn. Each step's K and V
-// rows (16 x 128 codes each) go from global memory straight into a per-wave
-// LDS ring (global_load_lds_dwordx4) kF8Ring steps ahead, so a wave only
-// waits on its own loads; the codes become the query's 2-byte type (exactly)
-// as the operands are read:
-//   * K as the A operand: lane l holds position l % 16 and codes
-//     32 ks + 8 (l / 16) .. + 7 of slice ks (ds_read_b64);
-//   * V^T as the A operand, via ds_read_b64_tr_b8: lane j of each 16-lane
-//     group gets byte j % 8 of the row addressed by group lane 2 y + j / 8 as
-//     its byte y. Group lane 2 y + h points at position 4 (l / 16) + y % 4,
-//     dimensions 16 (2 dd + y / 4) + 8 h, so lane j gets dimension 32 dd + j
-//     of its four positions in bytes 0-3 and dimension 32 dd + 16 + j in
-//     bytes 4-7: two dimension tiles per read.
-// The k order of P^T is the four positions 4 (l / 16) .. + 3 whose logits
-// the lane holds in S^T, so no weight crosses lanes. Rows of a tile are 128
-// bytes; the 16-byte unit u of row T sits at u ^ key(T), which keeps both
-// kinds of reads free of bank conflicts. Positions past the item's end, and
-// blocks whose table entry is out of range, load a zero chunk and are
-// masked; the online softmax is the lazy-reference one of the VALU item,
-// per column.
-#ifndef PA_F8_RING
-#define PA_F8_RING 2
-#endif
-constexpr int kF8Ring = PA_F8_RING;              // steps of loads in flight per wave
-constexpr int kF8Bufs = kF8Ring + 1;
-constexpr int kF8Step = 16;                      // positions per step
-constexpr int kF8Tile = kF8Step * 128;           // bytes of one step's K (or V) codes
-constexpr int kF8Loads = 2 * (kF8Tile / 1024);   // load instructions per step and wave
+// rows (16 rows of 128 elements each) go from global memory straight into a
+// per-wave LDS ring (global_load_lds_dwordx4 with the non-temporal hint)
+// MmaRows::kRing steps ahead, so a wave only waits on its own loads. The
+// operands are read as:
+//   * K as the A operand: lane l holds position l % 16 and elements
+//     32 ks + 8 (l / 16) .. + 7 of slice ks;
+//   * V^T as the A operand through the transposing LDS reads, which hand
+//     each lane one dimension of the four positions 4 (l / 16) .. + 3 (the
+//     lane layouts are in MmaRows).
+// The k order of P^T is those four positions, whose logits the lane holds in
+// S^T, so no weight crosses lanes. FP8 codes become the query's 2-byte type
+// (exactly) as the operands are read. Rows in LDS are swizzled: the 16-byte
+// unit u of row T sits at u ^ key(T), which keeps both kinds of reads free
+// of bank conflicts. Positions past the item's end, and blocks whose table
+// entry is out of range, load a zero chunk and are masked; the online
+// softmax is the lazy-reference one of the VALU item, per column.
+constexpr int kMmaStep = 16;                     // positions per step
 
-struct F8Ring {
-  alignas(16) uint8_t k[kDecodeWaves][kF8Bufs][kF8Tile];
-  alignas(16) uint8_t v[kDecodeWaves][kF8Bufs][kF8Tile];
-};
-
-template <int G>
-struct F8Lds {
-  int32_t tbl[kTableChunk];
-  union {
-    F8Ring ring;                                 // during the walk
-    float part[kDecodeWaves][G][128 + 2];        // after it (behind a barrier)
-  };
-};
-
-// Bijective on the 8 rows of each parity (K reads: 16 consecutive rows at
-// one unit), and rows 4q and 4q + 2 (or 4q + 1 and 4q + 3) differ in bit 2
-// (V reads: units 2 dd and 2 dd + 1 of four consecutive rows).
-__device__ __forceinline__ int f8_key(int T) { return ((T & 2) << 1) | ((T >> 2) & 3); }
-
-typedef int f8_v2i __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) f8_v2i f8_lds_v2i;
-typedef short f8_s4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f8_h4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 f8_lds_read8(uint32_t addr) {
-  const f8_v2i r = *reinterpret_cast<const f8_lds_v2i*>(mq_lds_ptr(addr));
+typedef int mma_v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) mma_v2i mma_lds_v2i;
+typedef short mma_s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mma_s4 mma_lds_s4;
+typedef _Float16 mma_h4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 mma_lds_read8(uint32_t addr) {
+  const mma_v2i r = *reinterpret_cast<const mma_lds_v2i*>(mq_lds_ptr(addr));
   return make_uint2((uint32_t)r.x, (uint32_t)r.y);
-}
-__device__ __forceinline__ uint2 f8_lds_read8_tr(uint32_t addr) {
-  const f8_v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<f8_lds_v2i*>(mq_lds_ptr(addr)));
-  return make_uint2((uint32_t)r.x, (uint32_t)r.y);
-}
-// Eight codes (two words) as a 16x16x32 operand of the query's 2-byte type.
-template <class QT>
-__device__ __forceinline__ u32x4_t f8_operand(uint2 w) {
-  return u32x4_t{Fp8Pair<QT>::template get<false>(w.x), Fp8Pair<QT>::template get<true>(w.x),
-                 Fp8Pair<QT>::template get<false>(w.y), Fp8Pair<QT>::template get<true>(w.y)};
 }
 // O^T += A . B with 16x16x16 operands (four values of the 2-byte type).
 template <class QT> struct Mma16;
 template <> struct Mma16<Fp16> {
   static __device__ __forceinline__ f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f8_h4, a),
-                                                 __builtin_bit_cast(f8_h4, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mma_h4, a),
+                                                 __builtin_bit_cast(mma_h4, b), c, 0, 0, 0);
   }
 };
 template <> struct Mma16<Bf16> {
   static __device__ __forceinline__ f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(f8_s4, a),
-                                                     __builtin_bit_cast(f8_s4, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mma_s4, a),
+                                                     __builtin_bit_cast(mma_s4, b), c, 0, 0, 0);
   }
 };
 
-template <class QT, int G, bool APP>
-__device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, int s, int p,
-                                                  F8Lds<G>& sm) {
+// What differs between an FP8 cache and one in the query's 2-byte type.
+template <class QT, class KT> struct MmaRows;
+
+// FP8: 128-byte rows (8 units). key: bijective on the 8 rows of each parity
+// (K reads: 16 consecutive rows at one unit), rows 4q and 4q + 2 (or 4q + 1
+// and 4q + 3) differ in bit 2 (V reads: units 2 dd and 2 dd + 1 of four
+// consecutive rows). V^T: ds_read_b64_tr_b8 hands lane j of a 16-lane group
+// byte j % 8 of the row addressed by group lane 2 y + j / 8 as its byte y;
+// group lane 2 y + h points at position 4 (l/16) + y % 4, dimensions
+// 16 (2 dd + y / 4) + 8 h, so one read gives lane j dimension 32 dd + j
+// (bytes 0-3) and 32 dd + 16 + j (bytes 4-7) of its four positions.
+template <class QT> struct MmaRows<QT, Fp8> {
+  static constexpr int kRowBytes = 128;
+  static constexpr int kRing = 2;                // steps of loads in flight per wave
+  static constexpr int kVReads = 4;              // transposing reads per step (2 tiles each)
+  static constexpr int kAppLanes = 8;            // lanes holding a row, 16 bytes each
+  static __device__ __forceinline__ int key(int T) { return ((T & 2) << 1) | ((T >> 2) & 3); }
+  static __device__ __forceinline__ uint32_t k_off(int j, int gq, int ks) {
+    return j * 128 + (((2 * ks + (gq >> 1)) ^ key(j)) << 4) + 8 * (gq & 1);
+  }
+  static __device__ __forceinline__ u32x4_t k_operand(uint32_t addr) {
+    const uint2 w = mma_lds_read8(addr);
+    return u32x4_t{Fp8Pair<QT>::template get<false>(w.x), Fp8Pair<QT>::template get<true>(w.x),
+                   Fp8Pair<QT>::template get<false>(w.y), Fp8Pair<QT>::template get<true>(w.y)};
+  }
+  static __device__ __forceinline__ uint32_t v_off(int j, int gq, int r) {
+    const int y = j >> 1;
+    const int T = 4 * gq + (y & 3);
+    return T * 128 + (((2 * r + (y >> 2)) ^ key(T)) << 4) + 8 * (j & 1);
+  }
+  // Dimension tiles 2 r and 2 r + 1.
+  static __device__ __forceinline__ void v_operands(uint32_t addr, uint2 (&v)[2]) {
+    const mma_v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        reinterpret_cast<mma_lds_v2i*>(mq_lds_ptr(addr)));
+    const uint32_t w0 = (uint32_t)t.x, w1 = (uint32_t)t.y;
+    v[0] = make_uint2(Fp8Pair<QT>::template get<false>(w0), Fp8Pair<QT>::template get<true>(w0));
+    v[1] = make_uint2(Fp8Pair<QT>::template get<false>(w1), Fp8Pair<QT>::template get<true>(w1));
+  }
+  // This lane's 16 bytes of the new token's K / V row, as the cache stores them.
+  static __device__ __forceinline__ u32x4_t app_row(const uint16_t* src, float scale) {
+    const typename Kv<QT, Fp8, 16>::row r = Kv<QT, Fp8, 16>::from_src(src, scale);
+    return u32x4_t{r[0], r[1], r[2], r[3]};
+  }
+};
+
+// 2-byte rows: 256 bytes (16 units); T = 4 a + b, key = (a >> 1) << 3 |
+// b << 1 | (a & 1): bijective on 16 rows (K reads), and for four consecutive
+// rows 4 a + b the keys differ above bit 0 (V reads: units 2 dt, 2 dt + 1).
+// V^T: ds_read_b64_tr_b16 hands lane j of a 16-lane group element j % 4 of
+// the row addressed by group lane 4 y + j / 4 as its element y; group lane
+// 4 y + q points at position 4 (l/16) + y, dimensions 16 dt + 4 q, so lane j
+// gets dimension 16 dt + j of its four positions.
+template <class QT> struct MmaRows<QT, QT> {
+  static constexpr int kRowBytes = 256;
+  static constexpr int kRing = 1;
+  static constexpr int kVReads = 8;
+  static constexpr int kAppLanes = 16;
+  static __device__ __forceinline__ int key(int T) {
+    return ((T >> 3) << 3) | ((T & 3) << 1) | ((T >> 2) & 1);
+  }
+  static __device__ __forceinline__ uint32_t k_off(int j, int gq, int ks) {
+    return j * 256 + (((4 * ks + gq) ^ key(j)) << 4);
+  }
+  static __device__ __forceinline__ u32x4_t k_operand(uint32_t addr) { return mq_lds_read16(mq_lds_ptr(addr)); }
+  static __device__ __forceinline__ uint32_t v_off(int j, int gq, int r) {
+    const int y = j >> 2, q = j & 3;
+    const int T = 4 * gq + y;
+    return T * 256 + (((2 * r + (q >> 1)) ^ key(T)) << 4) + 8 * (q & 1);
+  }
+  static __device__ __forceinline__ void v_operands(uint32_t addr, uint2 (&v)[1]) {
+    v[0] = mq_lds_read_tr16(mq_lds_ptr(addr));
+  }
+  static __device__ __forceinline__ u32x4_t app_row(const uint16_t* src, float) {
+    return *reinterpret_cast<const u32x4_t*>(src);
+  }
+};
+
+template <class QT, class KT>
+struct MmaLdsRing {
+  static constexpr int kTile = kMmaStep * MmaRows<QT, KT>::kRowBytes;
+  static constexpr int kBufs = MmaRows<QT, KT>::kRing + 1;
+  alignas(16) uint8_t k[kDecodeWaves][kBufs][kTile];
+  alignas(16) uint8_t v[kDecodeWaves][kBufs][kTile];
+};
+
+template <class QT, class KT, int G>
+struct MmaLds {
+  int32_t tbl[kTableChunk];
+  union {
+    MmaLdsRing<QT, KT> ring;                     // during the walk
+    float part[kDecodeWaves][G][128 + 2];        // after it (behind a barrier)
+  };
+};
+
+template <class QT, class KT, int G, bool APP>
+__device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, int s, int p,
+                                                MmaLds<QT, KT, G>& sm) {
   using S = Storage<QT>;
-  using KV = Kv<QT, Fp8, 16>;
+  using R = MmaRows<QT, KT>;
+  using KV = Kv<QT, KT, std::is_same<KT, Fp8>::value ? 16 : 8>;
   constexpr int D = 128;
   constexpr int NW = kDecodeWaves;
   constexpr int NT = NW * 64;
-  constexpr int RD = kF8Ring;
-  constexpr int NB = kF8Bufs;
+  constexpr int RD = R::kRing;
+  constexpr int NB = RD + 1;
+  constexpr int TILE = MmaLdsRing<QT, KT>::kTile;
+  constexpr int WL = TILE / 1024;                // wave loads per tile
+  constexpr int UNITS = R::kRowBytes / 16;
+  constexpr int VR = R::kVReads;
+  constexpr int VT = 8 / VR;                     // dimension tiles per transposing read
   static_assert(G >= 4 && G <= 16, "heads as matrix columns");
   const int Hkv = a.num_kv_heads;
   const int tid = threadIdx.x;
@@ -735,7 +797,7 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
   const int start = a.tok_offset + p * a.part_tokens;
   const int app = APP ? L - 1 : -1;
   if (start >= L) {
-    if (APP && p == 0) append_row<KV, 16, 8>(a, s, g, app, D, tid);
+    if (APP && p == 0) append_row<KV, 128 / R::kAppLanes, R::kAppLanes>(a, s, g, app, D, tid);
     if (p == 0 && !a.always_combine) {
       uint16_t* o = a.out + ((int64_t)s * a.num_q_heads + (int64_t)g * G) * D;
       for (int i = tid; i < G * D; i += NT) o[i] = 0;
@@ -752,9 +814,9 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
   const int lane = tid & 63;
   const int j = lane & 15;                     // head column / row of a 16-row operand
   const int gq = lane >> 4;
-  const int64_t tok_stride = (int64_t)Hkv * D;   // bytes between slots
-  const uint8_t* kc = static_cast<const uint8_t*>(a.kc) + (int64_t)g * D;
-  const uint8_t* vc = static_cast<const uint8_t*>(a.vc) + (int64_t)g * D;
+  const int64_t row_bytes = (int64_t)Hkv * R::kRowBytes;   // bytes between slots
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kc) + (int64_t)g * R::kRowBytes;
+  const uint8_t* vc = static_cast<const uint8_t*>(a.vc) + (int64_t)g * R::kRowBytes;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(kMqZeroChunk);
 
   // Q^T as the B operand: column j = head j of the group (zero past G),
@@ -768,25 +830,21 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
       qb[ks] = ok ? *reinterpret_cast<const u32x4_t*>(qs + 32 * ks + 8 * gq) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // LDS byte offsets within a tile. K reads: row j, slice ks. V^T reads: row
-  // 4 gq + y % 4 with y = j / 2, units 2 dd + y / 4, half j & 1.
-  uint32_t koff[4], voff[4];
+  uint32_t koff[4], voff[VR];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    koff[ks] = j * 128 + (((2 * ks + (gq >> 1)) ^ f8_key(j)) << 4) + 8 * (gq & 1);
-  {
-    const int y = j >> 1;
-    const int T = 4 * gq + (y & 3);
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = R::k_off(j, gq, ks);
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
-      voff[dd] = T * 128 + (((2 * dd + (y >> 2)) ^ f8_key(T)) << 4) + 8 * (j & 1);
-  }
+  for (int r = 0; r < VR; ++r) voff[r] = R::v_off(j, gq, r);
   // Loads: wave-load w of a tile fills bytes [1024 w, +1024): this lane's 16
-  // bytes are unit lane % 8 of row 8 w + lane / 8, which holds source unit
-  // (lane % 8) ^ key(row).
-  uint32_t lsrc[2];
+  // bytes are unit lane % UNITS of row (1024 w + 16 lane) / row bytes, which
+  // holds source unit (lane % UNITS) ^ key(row).
+  uint32_t lsrc[WL];
+  int lrow[WL];
 #pragma unroll
-  for (int w = 0; w < 2; ++w) lsrc[w] = (uint32_t)(((lane & 7) ^ f8_key(8 * w + (lane >> 3))) << 4);
+  for (int w = 0; w < WL; ++w) {
+    lrow[w] = (1024 * w + 16 * lane) / R::kRowBytes;
+    lsrc[w] = (uint32_t)(((lane % UNITS) ^ R::key(lrow[w])) << 4);
+  }
 
   const uint32_t kr0 = (uint32_t)(uintptr_t)&sm.ring.k[wave][0][0];
   const uint32_t vr0 = (uint32_t)(uintptr_t)&sm.ring.v[wave][0][0];
@@ -805,29 +863,28 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
   // wave's last (k >= mine) loads the zero chunk, so every step issues the
   // same number of loads. Returns whether the step's block entry is bad.
   auto issue = [&](int t0, int cb, int tend, int k, int mine) -> bool {
-    const int ts = t0 + kF8Step * (wave + NW * k);
+    const int ts = t0 + kMmaStep * (wave + NW * k);
     const int blk = k < mine ? __builtin_amdgcn_readfirstlane(sm.tbl[min((ts >> lbs) - cb, kTableChunk - 1)]) : -1;
     const bool okb = (uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks;
-    const uint32_t buf = (uint32_t)(k % NB) * kF8Tile;
+    const uint32_t buf = (uint32_t)(k % NB) * TILE;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int t = ts + 8 * w + (lane >> 3);  // this lane's position
+    for (int w = 0; w < WL; ++w) {
+      const int t = ts + lrow[w];              // this lane's position
       const bool ok = okb && t < tend;
-      const int64_t row = ((int64_t)blk * bs + (t & (bs - 1))) * tok_stride + lsrc[w];
+      const int64_t row = ((int64_t)blk * bs + (t & (bs - 1))) * row_bytes + lsrc[w];
       mq_lds_load16_nt(ok ? kc + row : zero, kr0 + buf + (uint32_t)w * 1024);
       mq_lds_load16_nt(ok ? vc + row : zero, vr0 + buf + (uint32_t)w * 1024);
     }
     return !okb;
   };
 
-  // One step from ring buffer buf: positions ts .. ts + 15, masked at tend.
+  // One step from ring buffer offset buf: positions ts .. ts + 15, masked at tend.
   auto compute = [&](int ts, int tend, uint32_t buf, bool bad) {
     const uint32_t kt = kr0 + buf;
     const uint32_t vt = vr0 + buf;
     f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      c = Mma<QT>::run(f8_operand<QT>(f8_lds_read8(kt + koff[ks])), qb[ks], c);
+    for (int ks = 0; ks < 4; ++ks) c = Mma<QT>::run(R::k_operand(kt + koff[ks]), qb[ks], c);
     float lg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[i] = ts + 4 * gq + i < tend && !bad ? c[i] * sl2 : -INFINITY;
@@ -848,10 +905,11 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
     lsum = S::dot2(pb.x, S::kOnes, lsum);
     lsum = S::dot2(pb.y, S::kOnes, lsum);
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      const u32x4_t v = f8_operand<QT>(f8_lds_read8_tr(vt + voff[dd]));
-      acc[2 * dd] = Mma16<QT>::run(make_uint2(v[0], v[1]), pb, acc[2 * dd]);
-      acc[2 * dd + 1] = Mma16<QT>::run(make_uint2(v[2], v[3]), pb, acc[2 * dd + 1]);
+    for (int r = 0; r < VR; ++r) {
+      uint2 v[VT];
+      R::v_operands(vt + voff[r], v);
+#pragma unroll
+      for (int e = 0; e < VT; ++e) acc[VT * r + e] = Mma16<QT>::run(v[e], pb, acc[VT * r + e]);
     }
   };
 
@@ -864,7 +922,7 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
     __syncthreads();
     const int t0 = cb << lbs;
     const int t1 = min(end_main, (cb + nb) << lbs);
-    const int nsteps = (t1 - t0 + kF8Step - 1) / kF8Step;
+    const int nsteps = (t1 - t0 + kMmaStep - 1) / kMmaStep;
     const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;   // uniform
     if (mine == 0) continue;
     bool bad[NB];
@@ -876,17 +934,17 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
         const int k = k0 + r;
         if (k >= mine) break;                    // uniform
         bad[(r + RD) % NB] = issue(t0, cb, t1, k + RD, mine);
-        mq_wait_loads<RD * kF8Loads>();          // step k's loads have landed
-        compute(t0 + kF8Step * (wave + NW * k), t1, (uint32_t)r * kF8Tile, bad[r]);
+        mq_wait_loads<RD * 2 * WL>();            // step k's loads have landed
+        compute(t0 + kMmaStep * (wave + NW * k), t1, (uint32_t)r * TILE, bad[r]);
       }
     }
     mq_wait_loads<0>();                          // the ring is free again
   }
 
   // The new token, in the wave that would take the next step: a step whose
-  // row 0 holds its codes (quantized as the cache write does) and whose other
-  // rows are zero, masked past app. Lanes 0-7 also store it at the slot.
-  const int app_wave = ((end_main - start + kF8Step - 1) / kF8Step) % NW;
+  // row 0 holds its row (as the cache stores it) and whose other rows are
+  // zero, masked past app. The row's lanes also store it at the slot.
+  const int app_wave = ((end_main - start + kMmaStep - 1) / kMmaStep) % NW;
   if (own_app && wave == app_wave) {             // uniform
     const int32_t blk = __builtin_amdgcn_readfirstlane(bt_row[app >> lbs]);
     const int32_t slot = blk * bs + (app & (bs - 1));
@@ -896,19 +954,21 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
       mq_lds_u32x4* kz = reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(kr0));
       mq_lds_u32x4* vz = reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(vr0));
 #pragma unroll
-      for (int i = 0; i < kF8Tile / 16 / 64; ++i) {
+      for (int i = 0; i < TILE / 16 / 64; ++i) {
         kz[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
         vz[lane + 64 * i] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      if (lane < 8) {
-        const int64_t src = ((int64_t)s * Hkv + g) * D + 16 * lane;
-        const typename KV::row kn = KV::from_src(a.k_new + src, a.k_scale_w);
-        const typename KV::row vn = KV::from_src(a.v_new + src, a.v_scale_w);
-        const int64_t dst = (int64_t)slot * tok_stride + 16 * lane;
-        KV::store(const_cast<uint8_t*>(kc) + dst, kn);
-        KV::store(const_cast<uint8_t*>(vc) + dst, vn);
-        kz[lane] = u32x4_t{kn[0], kn[1], kn[2], kn[3]};   // row 0: unit u at u ^ key(0) = u
-        vz[lane] = u32x4_t{vn[0], vn[1], vn[2], vn[3]};
+      if (lane < R::kAppLanes) {
+        // lane u holds elements 128 / kAppLanes * u ..: source unit u of row 0,
+        // which sits at unit u ^ key(0) = u
+        const int64_t src = ((int64_t)s * Hkv + g) * D + (128 / R::kAppLanes) * lane;
+        const u32x4_t kn = R::app_row(a.k_new + src, a.k_scale_w);
+        const u32x4_t vn = R::app_row(a.v_new + src, a.v_scale_w);
+        const int64_t dst = (int64_t)slot * row_bytes + 16 * lane;
+        *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(kc) + dst) = kn;
+        *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(vc) + dst) = vn;
+        kz[lane] = kn;
+        vz[lane] = vn;
       }
       compute(app, app + 1, 0, false);           // the wave's LDS accesses stay in order
     }
@@ -931,16 +991,26 @@ __device__ __forceinline__ void decode_item_f8mma(const DecodeParams& a, int g, 
   merge_waves<QT, D, G>(a, s, g, p, finish, sm.part, tid);
 }
 
+// Whether the matrix-core item serves a (cache type, head size, group):
+// grouped heads at head size 128 (FP8 GQA-8B 156 against 168 us for the
+// VALU item, bf16 GQA-8B 267 against 269, the long-context batch 172 against
+// 174; the cascade's short suffix items keep the VALU item, whose LDS
+// footprint lets all of them be resident at once).
+template <class KT, int D, int G>
+struct UseMmaItem {
+  static constexpr bool value = D == 128 && G >= 4;
+};
+
 // One work-group per item, in the partition kernel's grid order.
-template <class QT, int G, bool APP>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_f8mma_kernel(const DecodeParams a) {
-  __shared__ F8Lds<G> sm;
+template <class QT, class KT, int G, bool APP>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_mma_kernel(const DecodeParams a) {
+  __shared__ MmaLds<QT, KT, G> sm;
   int wg = blockIdx.x;
   const int g = wg % a.num_kv_heads;
   wg /= a.num_kv_heads;
   const int s = a.seq_major ? wg / a.num_parts : wg % a.num_seqs;
   const int p = a.seq_major ? wg % a.num_parts : wg / a.num_seqs;
-  decode_item_f8mma<QT, G, APP>(a, g, s, p, sm);
+  decode_item_mma<QT, KT, G, APP>(a, g, s, p, sm);
 }
 
 // One work-group per item. Work-groups are numbered kv head fastest. With
@@ -990,7 +1060,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
 // items, with or without stealing at the end) measured 3-9% slower.
 template <class DT, class KT, int D, int G, bool APP>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(const DecodeParams a) {
-  __shared__ DecodeLds<D, G> sm;
+  constexpr bool kMma = UseMmaItem<KT, D, G>::value;
+  __shared__ typename std::conditional<kMma, MmaLds<DT, KT, G>, DecodeLds<D, G>>::type sm;
   __shared__ int s_item[2];
   const int Hkv = a.num_kv_heads;
   const int total = Hkv * a.num_seqs * a.num_parts;
@@ -1002,7 +1073,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_persistent_kernel(co
     const int g = it % Hkv;
     const int s = (it / Hkv) % a.num_seqs;
     const int p = it / (Hkv * a.num_seqs);
-    decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
+    if constexpr (kMma)
+      decode_item_mma<DT, KT, G, APP>(a, g, s, p, sm);
+    else
+      decode_item<DT, KT, D, G, APP, kTileTokens>(a, g, s, p, sm);
     if (!counted) {
       // The next item writes its waves' sums into sm.part, which threads of
       // this item may still be reading in the cross-wave merge: an item whose
@@ -1239,11 +1313,8 @@ hipError_t launch_dga(const DecodeParams& a, hipStream_t st) {
   } else {
     DecodeParams b = a;
     b.sched = nullptr;                   // the combine leaves the scheduler words alone
-    if constexpr (std::is_same<KT, Fp8>::value && D == 128 && G >= 4) {
-      // FP8 cache with grouped heads: the matrix-core item (non-temporal
-      // LDS loads, two steps in flight: 156 against 168 us for the VALU
-      // item on the FP8 GQA-8B batch).
-      hipLaunchKernelGGL((decode_f8mma_kernel<DT, G, APP>), dim3((uint32_t)nwg),
+    if constexpr (UseMmaItem<KT, D, G>::value) {
+      hipLaunchKernelGGL((decode_mma_kernel<DT, KT, G, APP>), dim3((uint32_t)nwg),
                          dim3(kDecodeWaves * 64), 0, st, b);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !combine) return e;

@@ -755,35 +755,37 @@ template <class QT> struct MmaRows<QT, QT> {
   }
 };
 
-template <class QT, class KT>
+template <class QT, class KT, int RD>
 struct MmaLdsRing {
   static constexpr int kTile = kMmaStep * MmaRows<QT, KT>::kRowBytes;
-  static constexpr int kBufs = MmaRows<QT, KT>::kRing + 1;
+  static constexpr int kBufs = RD + 1;
   alignas(16) uint8_t k[kDecodeWaves][kBufs][kTile];
   alignas(16) uint8_t v[kDecodeWaves][kBufs][kTile];
 };
 
-template <class QT, class KT, int G>
+template <class QT, class KT, int G, int RD = MmaRows<QT, KT>::kRing>
 struct MmaLds {
   int32_t tbl[kTableChunk];
   union {
-    MmaLdsRing<QT, KT> ring;                     // during the walk
+    MmaLdsRing<QT, KT, RD> ring;                 // during the walk
     float part[kDecodeWaves][G][128 + 2];        // after it (behind a barrier)
   };
 };
 
-template <class QT, class KT, int G, bool APP>
+// RD: steps of loads in flight per wave. With RD = 0 a step's K loads are
+// waited for first, its logits and weights computed while its V loads
+// land, and only then V waited for.
+template <class QT, class KT, int G, bool APP, int RD = MmaRows<QT, KT>::kRing>
 __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, int s, int p,
-                                                MmaLds<QT, KT, G>& sm) {
+                                                MmaLds<QT, KT, G, RD>& sm) {
   using S = Storage<QT>;
   using R = MmaRows<QT, KT>;
   using KV = Kv<QT, KT, std::is_same<KT, Fp8>::value ? 16 : 8>;
   constexpr int D = 128;
   constexpr int NW = kDecodeWaves;
   constexpr int NT = NW * 64;
-  constexpr int RD = R::kRing;
   constexpr int NB = RD + 1;
-  constexpr int TILE = MmaLdsRing<QT, KT>::kTile;
+  constexpr int TILE = MmaLdsRing<QT, KT, RD>::kTile;
   constexpr int WL = TILE / 1024;                // wave loads per tile
   constexpr int UNITS = R::kRowBytes / 16;
   constexpr int VR = R::kVReads;
@@ -867,19 +869,26 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
     const int blk = k < mine ? __builtin_amdgcn_readfirstlane(sm.tbl[min((ts >> lbs) - cb, kTableChunk - 1)]) : -1;
     const bool okb = (uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks;
     const uint32_t buf = (uint32_t)(k % NB) * TILE;
+    int64_t row[WL];
+    bool ok[WL];
 #pragma unroll
     for (int w = 0; w < WL; ++w) {
       const int t = ts + lrow[w];              // this lane's position
-      const bool ok = okb && t < tend;
-      const int64_t row = ((int64_t)blk * bs + (t & (bs - 1))) * row_bytes + lsrc[w];
-      mq_lds_load16_nt(ok ? kc + row : zero, kr0 + buf + (uint32_t)w * 1024);
-      mq_lds_load16_nt(ok ? vc + row : zero, vr0 + buf + (uint32_t)w * 1024);
+      ok[w] = okb && t < tend;
+      row[w] = ((int64_t)blk * bs + (t & (bs - 1))) * row_bytes + lsrc[w];
     }
+#pragma unroll
+    for (int w = 0; w < WL; ++w)               // all of K first, then V
+      mq_lds_load16_nt(ok[w] ? kc + row[w] : zero, kr0 + buf + (uint32_t)w * 1024);
+#pragma unroll
+    for (int w = 0; w < WL; ++w)
+      mq_lds_load16_nt(ok[w] ? vc + row[w] : zero, vr0 + buf + (uint32_t)w * 1024);
     return !okb;
   };
 
-  // One step from ring buffer offset buf: positions ts .. ts + 15, masked at tend.
-  auto compute = [&](int ts, int tend, uint32_t buf, bool bad) {
+  // One step from ring buffer offset buf: positions ts .. ts + 15, masked at
+  // tend. wait_v runs between the weights and the V products.
+  auto compute = [&](int ts, int tend, uint32_t buf, bool bad, auto wait_v) {
     const uint32_t kt = kr0 + buf;
     const uint32_t vt = vr0 + buf;
     f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -904,6 +913,7 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
     pb.y = Mma<QT>::pack(fast_exp2(lg[2] - mn), fast_exp2(lg[3] - mn));
     lsum = S::dot2(pb.x, S::kOnes, lsum);
     lsum = S::dot2(pb.y, S::kOnes, lsum);
+    wait_v();
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
       uint2 v[VT];
@@ -925,17 +935,25 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
     const int nsteps = (t1 - t0 + kMmaStep - 1) / kMmaStep;
     const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;   // uniform
     if (mine == 0) continue;
-    bool bad[NB];
+    if constexpr (RD == 0) {
+      for (int k = 0; k < mine; ++k) {
+        const bool bad = issue(t0, cb, t1, k, mine);
+        mq_wait_loads<WL>();                     // K has landed (V was issued after it)
+        compute(t0 + kMmaStep * (wave + NW * k), t1, 0u, bad, [] { mq_wait_loads<0>(); });
+      }
+    } else {
+      bool bad[NB];
 #pragma unroll
-    for (int r = 0; r < RD; ++r) bad[r] = issue(t0, cb, t1, r, mine);
-    for (int k0 = 0; k0 < mine; k0 += NB) {
+      for (int r = 0; r < RD; ++r) bad[r] = issue(t0, cb, t1, r, mine);
+      for (int k0 = 0; k0 < mine; k0 += NB) {
 #pragma unroll
-      for (int r = 0; r < NB; ++r) {
-        const int k = k0 + r;
-        if (k >= mine) break;                    // uniform
-        bad[(r + RD) % NB] = issue(t0, cb, t1, k + RD, mine);
-        mq_wait_loads<RD * 2 * WL>();            // step k's loads have landed
-        compute(t0 + kMmaStep * (wave + NW * k), t1, (uint32_t)r * TILE, bad[r]);
+        for (int r = 0; r < NB; ++r) {
+          const int k = k0 + r;
+          if (k >= mine) break;                  // uniform
+          bad[(r + RD) % NB] = issue(t0, cb, t1, k + RD, mine);
+          mq_wait_loads<RD * 2 * WL>();          // step k's loads have landed
+          compute(t0 + kMmaStep * (wave + NW * k), t1, (uint32_t)r * TILE, bad[r], [] {});
+        }
       }
     }
     mq_wait_loads<0>();                          // the ring is free again
@@ -970,7 +988,7 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
         kz[lane] = kn;
         vz[lane] = vn;
       }
-      compute(app, app + 1, 0, false);           // the wave's LDS accesses stay in order
+      compute(app, app + 1, 0, false, [] {});    // the wave's LDS accesses stay in order
     }
   }
 
@@ -1269,8 +1287,15 @@ template <class DT, int D, int G, bool APP, int TILE>
 __global__ __launch_bounds__(kDecodeWaves * 64, FusedWavesPerEu<G>::value) void cascade_fused_kernel(
     const DecodeParams a) {
   static_assert(cascade_waves(D) == kDecodeWaves, "one work-group shape for both kinds");
+  // The suffix items: the matrix-core item without a ring (one buffer, 33 KB
+  // with the table, so that all suffix items of the prefix-shared batch stay
+  // resident: 42.2-42.8 against 42.8-43.1 us for the VALU item) for grouped
+  // heads at head size 128, else the VALU item.
+  constexpr bool kMma = UseMmaItem<DT, D, G>::value;
+  using SuffixLds =
+      typename std::conditional<kMma, MmaLds<DT, DT, G, 0>, DecodeLds<D, G>>::type;
   __shared__ union {
-    DecodeLds<D, G> dec;
+    SuffixLds dec;
     PrefixLds<D, kFusedPrefixRing> pre;
   } sm;
   const int Hkv = a.num_kv_heads;
@@ -1282,7 +1307,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, FusedWavesPerEu<G>::value) void 
   }
   const int g = wg % Hkv;
   wg /= Hkv;
-  decode_item<DT, DT, D, G, APP, TILE>(a, g, wg % a.num_seqs, wg / a.num_seqs, sm.dec);
+  if constexpr (kMma)
+    decode_item_mma<DT, DT, G, APP, 0>(a, g, wg % a.num_seqs, wg / a.num_seqs, sm.dec);
+  else
+    decode_item<DT, DT, D, G, APP, TILE>(a, g, wg % a.num_seqs, wg / a.num_seqs, sm.dec);
 }
 
 template <class DT, int D>

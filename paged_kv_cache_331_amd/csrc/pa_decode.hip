@@ -681,10 +681,11 @@ template <> struct Mma16<Bf16> {
 // What differs between an FP8 cache and one in the query's 2-byte type.
 template <class QT, class KT> struct MmaRows;
 
-// FP8: 128-byte rows (8 units). key: bijective on the 8 rows of each parity
-// (K reads: 16 consecutive rows at one unit), rows 4q and 4q + 2 (or 4q + 1
-// and 4q + 3) differ in bit 2 (V reads: units 2 dd and 2 dd + 1 of four
-// consecutive rows). V^T: ds_read_b64_tr_b8 hands lane j of a 16-lane group
+// FP8: 128-byte rows (8 units), two to a 256-byte pass over the banks.
+// key: bijective on the 8 rows of each parity (K reads: 16 consecutive rows
+// at one unit, two halves), and key >> 1 distinct over the rows of one
+// parity among 8 aligned rows (V reads of two 16-lane groups together:
+// units 2 dd and 2 dd + 1 of rows 4 q .. 4 q + 7). V^T: ds_read_b64_tr_b8 hands lane j of a 16-lane group
 // byte j % 8 of the row addressed by group lane 2 y + j / 8 as its byte y;
 // group lane 2 y + h points at position 4 (l/16) + y % 4, dimensions
 // 16 (2 dd + y / 4) + 8 h, so one read gives lane j dimension 32 dd + j
@@ -694,7 +695,7 @@ template <class QT> struct MmaRows<QT, Fp8> {
   static constexpr int kRing = 2;                // steps of loads in flight per wave
   static constexpr int kVReads = 4;              // transposing reads per step (2 tiles each)
   static constexpr int kAppLanes = 8;            // lanes holding a row, 16 bytes each
-  static __device__ __forceinline__ int key(int T) { return ((T & 2) << 1) | ((T >> 2) & 3); }
+  static __device__ __forceinline__ int key(int T) { return (((T >> 1) & 3) << 1) | ((T >> 3) & 1); }
   static __device__ __forceinline__ uint32_t k_off(int j, int gq, int ks) {
     return j * 128 + (((2 * ks + (gq >> 1)) ^ key(j)) << 4) + 8 * (gq & 1);
   }
@@ -723,9 +724,10 @@ template <class QT> struct MmaRows<QT, Fp8> {
   }
 };
 
-// 2-byte rows: 256 bytes (16 units); T = 4 a + b, key = (a >> 1) << 3 |
-// b << 1 | (a & 1): bijective on 16 rows (K reads), and for four consecutive
-// rows 4 a + b the keys differ above bit 0 (V reads: units 2 dt, 2 dt + 1).
+// 2-byte rows: 256 bytes (16 units, one pass over the banks). key:
+// bijective on 16 rows (K reads: 16 rows at one unit), and key >> 1
+// distinct over 8 aligned rows (V reads of two 16-lane groups together:
+// units 2 dt and 2 dt + 1 of rows 4 q .. 4 q + 7).
 // V^T: ds_read_b64_tr_b16 hands lane j of a 16-lane group element j % 4 of
 // the row addressed by group lane 4 y + j / 4 as its element y; group lane
 // 4 y + q points at position 4 (l/16) + y, dimensions 16 dt + 4 q, so lane j
@@ -735,9 +737,7 @@ template <class QT> struct MmaRows<QT, QT> {
   static constexpr int kRing = 1;
   static constexpr int kVReads = 8;
   static constexpr int kAppLanes = 16;
-  static __device__ __forceinline__ int key(int T) {
-    return ((T >> 3) << 3) | ((T & 3) << 1) | ((T >> 2) & 1);
-  }
+  static __device__ __forceinline__ int key(int T) { return ((T & 7) << 1) | ((T >> 3) & 1); }
   static __device__ __forceinline__ uint32_t k_off(int j, int gq, int ks) {
     return j * 256 + (((4 * ks + gq) ^ key(j)) << 4);
   }

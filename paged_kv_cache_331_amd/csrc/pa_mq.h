@@ -197,8 +197,11 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 }
 
 // Attend every row of the work-group to positions [c0, kend) of kv head g.
-// slot_of(t) gives position t's physical slot (int32, as the slot mapping
-// defines it) for c0 <= t < kend, or -1 for a skipped block, read as zeros.
+// blk_of(t) gives the physical block of position t (c0 <= t < kend, asked
+// with a wave-uniform t), or -1 for a skipped block, read as zeros;
+// position t sits at slot blk * bs + t % bs. c0 is a multiple of 16 and of
+// bs (>= 16), so the rows one wave's load slice covers (4 at head size 128,
+// 8 at 64) never straddle a block.
 // Keys >= row_end[b] are masked for this lane's row of block b; every
 // position below kend must hold finite data (a position some row of the
 // work-group may use). Must be reached by all threads of the work-group with
@@ -209,11 +212,12 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 // before the softmax (32 fewer VGPRs at head size 128, for callers that
 // share a register budget).
 template <class DT, int D, int RB, int W = kMqWaves, int RD = kMqRing, bool LEAN = false,
-          class SlotOf>
+          class BlkOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
                                           MqLds<D, RD + 1>& lds, const uint16_t* kc, const uint16_t* vc,
                                           int64_t tok_stride, int g, int c0, int kend,
-                                          const int (&row_end)[RB], float sl2, SlotOf slot_of) {
+                                          const int (&row_end)[RB], float sl2, int bs,
+                                          BlkOf blk_of) {
   constexpr int KS = D / 32;
   constexpr int DTILES = D / 16;
   constexpr int CH = D / 8;                    // 16-byte chunks of a row
@@ -233,8 +237,6 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   const uint16_t* vbase = vc + (int64_t)g * D;
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kMqZeroChunk);
   const uint32_t stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^31 elements
-  // Element offset of a slot's row: one 32 x 32 -> 64-bit multiply.
-  auto row_off = [&](int sl) -> uint64_t { return (uint64_t)(uint32_t)sl * stride32; };
 
   // LDS byte addresses. Loads: slice u of this wave covers 16-byte units
   // 64 * (wave + W * u) + lane of a tile, i.e. key row dr[u], chunk dc[u].
@@ -246,14 +248,19 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   constexpr int VU = D / 16;                   // 32-byte units per row
   constexpr int RPB = 128 / D;                 // rows per 256 bytes (one pass over the banks)
   auto vsw = [](int r) { return (r / RPB) % VU; };
-  int dr[SPW], dc[SPW], dcv[SPW];
+  // Per slice: dr the lane's key row, lk / lv its element offset from the
+  // slice's first row (row within the slice times the row stride, plus the
+  // source chunk that lands at this lane's 16 bytes).
+  int dr[SPW];
+  uint32_t lk[SPW], lv[SPW];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int unit = 64 * (wave + W * u) + lane;
     const int cp = unit % CH;
     dr[u] = unit / CH;
-    dc[u] = cp ^ (dr[u] % CH16);
-    dcv[u] = 2 * ((cp >> 1) ^ vsw(dr[u])) + (cp & 1);
+    const uint32_t lrow = (uint32_t)(lane / CH) * stride32;
+    lk[u] = lrow + (uint32_t)((cp ^ (dr[u] % CH16)) * 8);
+    lv[u] = lrow + (uint32_t)((2 * ((cp >> 1) ^ vsw(dr[u])) + (cp & 1)) * 8);
   }
   // A operand of S^T: key row 16 kt + j, chunk grp + 4 ks (kt adds 16 rows).
   const mq_lds_byte* ka[KS];
@@ -288,16 +295,18 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   wmax = __builtin_amdgcn_readfirstlane(wmax);
 
   // Step at t0 into LDS buffer buf; positions >= kend and skipped blocks
-  // read the zero chunk (slot_of is only asked for positions in [c0, kend)).
+  // read the zero chunk (blk_of is only asked for positions in [c0, kend)).
+  // A slice's block and the slot of its first row are wave-uniform.
   auto issue = [&](int t0, int buf) {
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
-      const int t = t0 + dr[u];
-      const int sl = t < kend ? slot_of(max(min(t, kend - 1), c0)) : -1;
-      const uint64_t off = row_off(sl >= 0 ? sl : 0);
+      const int tf = t0 + (64 * (wave + W * u)) / CH;      // the slice's first position
+      const int blk = __builtin_amdgcn_readfirstlane(tf < kend ? blk_of(tf) : -1);
+      const bool ok = blk >= 0 && t0 + dr[u] < kend;
+      const uint64_t base = (uint64_t)(uint32_t)(blk * bs + (tf & (bs - 1))) * stride32;
       const uint32_t dst = (uint32_t)(wave + W * u) * 1024 + (uint32_t)buf * TILE;
-      mq_lds_load16(sl >= 0 ? kbase + off + dc[u] * 8 : zero, k0 + dst);
-      mq_lds_load16(sl >= 0 ? vbase + off + dcv[u] * 8 : zero, v0 + dst);
+      mq_lds_load16(ok ? kbase + base + lk[u] : zero, k0 + dst);
+      mq_lds_load16(ok ? vbase + base + lv[u] : zero, v0 + dst);
     }
   };
   auto compute = [&](int t0, int buf) {

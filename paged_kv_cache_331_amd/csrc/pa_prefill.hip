@@ -125,13 +125,10 @@ __global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(co
       s_tbl[i] = (uint64_t)(uint32_t)blk < (uint64_t)p.num_blocks ? blk : -1;
     }
     __syncthreads();
-    auto slot_of = [&](int t) -> int {
-      const int blk = s_tbl[(t >> lbs) - b0];
-      return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
-    };
+    auto blk_of = [&](int t) -> int { return s_tbl[(t >> lbs) - b0]; };
     mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
                          static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
-                         fabsf(p.scale_log2), slot_of);   // ends with a barrier: s_tbl is free again
+                         fabsf(p.scale_log2), bs, blk_of);   // ends with a barrier: s_tbl is free again
   }
 
 #pragma unroll

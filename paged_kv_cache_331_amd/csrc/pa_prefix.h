@@ -115,13 +115,10 @@ __device__ __forceinline__ void cascade_prefix_wg(const DecodeParams& a, int wg,
   }
   MqState<D, RB> st;
   st.init();
-  auto slot_of = [&](int t) -> int {
-    const int blk = s_tbl[(t >> lbs) - b0];
-    return blk < 0 ? -1 : blk * bs + (t & (bs - 1));
-  };
+  auto blk_of = [&](int t) -> int { return s_tbl[(t >> lbs) - b0]; };
   mq_attend<DT, D, RB, W, RD, LEAN>(st, qb, sm.mq, static_cast<const uint16_t*>(a.kc),
                           static_cast<const uint16_t*>(a.vc), (int64_t)Hkv * D, g, c0, kend,
-                          row_end, fabsf(a.scale_log2), slot_of);
+                          row_end, fabsf(a.scale_log2), bs, blk_of);
 
   // Partial of this chunk for each row: (reference max, sum of weights,
   // unnormalised O), consistent with one another whatever the reference.

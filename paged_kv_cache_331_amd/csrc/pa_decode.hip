@@ -839,13 +839,16 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
   for (int r = 0; r < VR; ++r) voff[r] = R::v_off(j, gq, r);
   // Loads: wave-load w of a tile fills bytes [1024 w, +1024): this lane's 16
   // bytes are unit lane % UNITS of row (1024 w + 16 lane) / row bytes, which
-  // holds source unit (lane % UNITS) ^ key(row).
-  uint32_t lsrc[WL];
+  // holds source unit (lane % UNITS) ^ key(row). The rows of one wave-load
+  // (8 at FP8, 4 at 2 bytes) lie in one block, so its first row's slot is
+  // wave-uniform; loff is this lane's byte offset from that row.
+  uint32_t loff[WL];
   int lrow[WL];
 #pragma unroll
   for (int w = 0; w < WL; ++w) {
     lrow[w] = (1024 * w + 16 * lane) / R::kRowBytes;
-    lsrc[w] = (uint32_t)(((lane % UNITS) ^ R::key(lrow[w])) << 4);
+    loff[w] = (uint32_t)(lrow[w] - (1024 * w) / R::kRowBytes) * (uint32_t)row_bytes +
+              (uint32_t)(((lane % UNITS) ^ R::key(lrow[w])) << 4);
   }
 
   const uint32_t kr0 = (uint32_t)(uintptr_t)&sm.ring.k[wave][0][0];
@@ -873,9 +876,9 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
     bool ok[WL];
 #pragma unroll
     for (int w = 0; w < WL; ++w) {
-      const int t = ts + lrow[w];              // this lane's position
-      ok[w] = okb && t < tend;
-      row[w] = ((int64_t)blk * bs + (t & (bs - 1))) * row_bytes + lsrc[w];
+      const int tw = ts + (1024 * w) / R::kRowBytes;      // the wave-load's first position
+      ok[w] = okb && ts + lrow[w] < tend;
+      row[w] = ((int64_t)blk * bs + (tw & (bs - 1))) * row_bytes + loff[w];
     }
 #pragma unroll
     for (int w = 0; w < WL; ++w)               // all of K first, then V

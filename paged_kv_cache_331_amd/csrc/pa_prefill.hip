@@ -62,8 +62,19 @@ __global__ __launch_bounds__(kSlotThreads) void prefill_slot_kernel(const Prefil
   p.slots[a + i] = row[pos / p.block_size] * p.block_size + pos % p.block_size;
 }
 
+// Grouped heads run three work-groups per CU, with the core's lean form (V
+// fragments read just before their products) and a register cap that spills
+// a few values: chunked GQA prefill 177-179 against 184-188 us. One query
+// head per kv head keeps two per CU (the same form measured 93-95 against
+// 92-93 us on the MHA prompts).
+template <int G> struct PrefillOccupancy {
+  static constexpr bool kLean = G >= 4;
+  static constexpr int kWavesPerEu = G >= 4 ? 3 : 1;   // 1: no bound (two fit)
+};
+
 template <class DT, int D, int G>
-__global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(PrefillWaves<D>::value * 64, PrefillOccupancy<G>::kWavesPerEu)
+void prefill_kernel(const PrefillParams p) {
   using S = Storage<DT>;
   constexpr int W = PrefillWaves<D>::value;
   constexpr int NT = W * 64;
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(PrefillWaves<D>::value * 64) void prefill_kernel(co
     }
     __syncthreads();
     auto blk_of = [&](int t) -> int { return s_tbl[(t >> lbs) - b0]; };
-    mq_attend<DT, D, RB, W>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
+    mq_attend<DT, D, RB, W, kMqRing, PrefillOccupancy<G>::kLean>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
                          static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
                          fabsf(p.scale_log2), bs, blk_of);   // ends with a barrier: s_tbl is free again
   }

@@ -1256,18 +1256,33 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_few_kernel(const
   const float* pm = a.ws_m + oh * a.part_stride;
   const float* pl = a.ws_l + oh * a.part_stride;
   const float4* po = reinterpret_cast<const float4*>(a.ws_o + oh * a.part_stride * D) + c;
+  // Every partial's loads are issued before any is used (np <= kFewParts).
+  float mv[kFewParts], lv[kFewParts];
+  float4 ov[kFewParts];
+#pragma unroll
+  for (int q = 0; q < kFewParts; ++q) {
+    if (q < np) {
+      mv[q] = pm[q];
+      lv[q] = pl[q];
+      ov[q] = po[(int64_t)q * CH];
+    }
+  }
   float M = kEmptyMax;
-  for (int q = 0; q < np; ++q) M = fmaxf(M, pm[q]);
+#pragma unroll
+  for (int q = 0; q < kFewParts; ++q)
+    if (q < np) M = fmaxf(M, mv[q]);
   float den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q = 0; q < np; ++q) {
-    const float w = fast_exp2(pm[q] - M);
-    const float4 x = po[(int64_t)q * CH];
-    den = fmaf(w, pl[q], den);
-    acc.x = fmaf(w, x.x, acc.x);
-    acc.y = fmaf(w, x.y, acc.y);
-    acc.z = fmaf(w, x.z, acc.z);
-    acc.w = fmaf(w, x.w, acc.w);
+#pragma unroll
+  for (int q = 0; q < kFewParts; ++q) {
+    if (q < np) {
+      const float w = fast_exp2(mv[q] - M);
+      den = fmaf(w, lv[q], den);
+      acc.x = fmaf(w, ov[q].x, acc.x);
+      acc.y = fmaf(w, ov[q].y, acc.y);
+      acc.z = fmaf(w, ov[q].z, acc.z);
+      acc.w = fmaf(w, ov[q].w, acc.w);
+    }
   }
   const float inv = 1.f / den;
   uint2 packed;

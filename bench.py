@@ -134,7 +134,8 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: st
     rec = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_fetch,
            "write_scale": f_write, "kernels": {}}
     total = 0.0
-    for tag in ("cascade_fused_kernel", "decode_partition_kernel", "decode_persistent_kernel",
+    for tag in ("cascade_fused_kernel", "decode_partition_kernel", "decode_mma_kernel",
+                "decode_persistent_kernel",
                 "decode_reduce_kernel", "decode_reduce_few_kernel"):
         m = lambda k, tag=tag: tag in k
         try:
@@ -292,7 +293,7 @@ def cold_calls(step, reps: int = 20, flush_bytes: int = 1 << 30) -> list:
     the back-to-back steps of the main loop. Returns milliseconds per call.
     """
     import torch
-    buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    buf = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")   # summed as is: a pure read
     evs = []
     for _ in range(reps):
         buf.sum()

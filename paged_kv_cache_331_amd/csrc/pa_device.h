@@ -123,6 +123,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_t load_stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
+// 16 bytes through a global-address-space pointer: a load whose address is
+// chosen between a buffer and a constant (the zero chunk) stays a global
+// load instead of a flat one.
+__device__ __forceinline__ u32x4_t load_global16(const void* p) {
+  return *(const __attribute__((address_space(1))) u32x4_t*)p;
+}
 __device__ __forceinline__ u32x2_t load_stream8(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }

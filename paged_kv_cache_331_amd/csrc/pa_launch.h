@@ -28,7 +28,7 @@ struct DecodeParams {
   int32_t max_blocks_per_seq;
   int64_t num_blocks;
   int32_t part_tokens;      // tokens per partition (multiple of 16 and of block_size);
-                            // at least max_context_len when there is no split
+                            // max_context_len (any value) when there is no split
   int32_t num_parts;        // partitions per sequence in the grid (1: no split, no workspace)
   int32_t seq_major;        // grid order: 1 = sequence index slowest, 0 = partition slowest
   int32_t tok_offset;       // first position the partitions cover (a multiple of block_size;

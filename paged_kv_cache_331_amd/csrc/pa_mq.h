@@ -183,16 +183,26 @@ template <bool B> struct MqFlag { static constexpr bool value = B; };
 // Q^T as the B operand: this lane's query row q (D elements), k = 8*grp + 32*ks.
 // With neg set every element's sign is flipped (exact in both 2-byte types):
 // q.k * scale = (-q).k * |scale| for a negative scale, and the core takes
-// scales >= 0 only.
-template <int D>
+// scales >= 0 only. A row outside the batch (ok false) holds zeros. UNCOND:
+// such a row reads the zero chunk instead of skipping its loads, so that no
+// load is conditional and none is waited for before the loads the caller
+// issues next.
+template <int D, bool UNCOND = false>
 __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t* q, bool ok,
                                           bool neg) {
   const int grp = (threadIdx.x & 63) >> 4;
   const uint32_t flip = neg ? 0x80008000u : 0u;
+  if constexpr (UNCOND) {
+    const uint16_t* src = ok ? q + 8 * grp : reinterpret_cast<const uint16_t*>(kMqZeroChunk);
+    const int step = ok ? 32 : 0;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    qb[ks] = ok ? *reinterpret_cast<const u32x4_t*>(q + 8 * grp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-    qb[ks] ^= flip;
+    for (int ks = 0; ks < D / 32; ++ks) qb[ks] = load_global16(src + step * ks) ^ flip;
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qb[ks] = ok ? *reinterpret_cast<const u32x4_t*>(q + 8 * grp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      qb[ks] ^= flip;
+    }
   }
 }
 

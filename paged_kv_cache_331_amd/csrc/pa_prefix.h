@@ -65,23 +65,41 @@ __device__ __forceinline__ void cascade_prefix_wg(const DecodeParams& a, int wg,
   const int R = a.num_seqs * G;          // query rows of kv head g
   const int c0 = chunk * kPrefixChunk;
   const int c1 = min(a.prefix_len, c0 + kPrefixChunk);
+  const int lbs = a.log2_block_size;
+  const int bs = a.block_size;
+  const int b0 = c0 >> lbs;
+  const int nb = (c1 - c0 + bs - 1) >> lbs;
+  static_assert(kPrefixChunk / 16 <= NT, "one table entry per thread");
   // Row block b of this wave: row rt * rows-per-work-group + wave * 16 * RB +
   // 16 * b + j, a (sequence, query head) pair of kv head g.
-  int s[RB], h[RB], limit[RB];
+  int s[RB], h[RB];
   bool row_ok[RB];
-  int wl = 0;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int r = rt * cascade_rows_per_wg(D) + wave * 16 * RB + 16 * b + j;
     row_ok[b] = r < R;
     s[b] = row_ok[b] ? r / G : 0;
     h[b] = g * G + (row_ok[b] ? r % G : 0);
-    limit[b] = 0;                        // keys this row may use: min(L, prefix_len)
-    if (row_ok[b]) {
-      int L = a.lens[s[b]];
-      L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-      limit[b] = min(L, a.prefix_len);
-    }
+  }
+  // The lengths, the queries and the chunk's table entries do not depend on
+  // one another, so their loads are in flight together. Row 0 of the tables
+  // holds the prefix.
+  int len[RB];                           // s[b] = 0 outside the batch: no load is conditional
+#pragma unroll
+  for (int b = 0; b < RB; ++b) len[b] = a.lens[s[b]];
+  u32x4_t qb[RB][D / 32];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+    mq_load_q<D, true>(qb[b], a.q + ((int64_t)s[b] * a.num_q_heads + h[b]) * D, row_ok[b],
+                       a.scale_log2 < 0.f);
+  const int tb = a.bt[b0 + min(tid, nb - 1)];   // nb >= 1: the chunk starts below prefix_len
+
+  int limit[RB];                         // keys each row may use: min(L, prefix_len)
+  int wl = 0;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int L = len[b] < 0 ? 0 : (len[b] > a.len_cap ? a.len_cap : len[b]);
+    limit[b] = row_ok[b] ? min(L, a.prefix_len) : 0;
     wl = max(wl, limit[b]);
   }
   // The work-group's largest limit: K/V rows at or past it are not positions
@@ -89,30 +107,17 @@ __device__ __forceinline__ void cascade_prefix_wg(const DecodeParams& a, int wg,
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) wl = max(wl, __shfl_xor(wl, o));
   if (lane == 0) s_limit[wave] = wl;
-
-  const int lbs = a.log2_block_size;
-  const int bs = a.block_size;
-  const int b0 = c0 >> lbs;
-  const int nb = (c1 - c0 + bs - 1) >> lbs;
-  for (int i = tid; i < nb; i += NT) {    // row 0 of the tables holds the prefix
-    const int blk = a.bt[b0 + i];
-    s_tbl[i] = (uint64_t)(uint32_t)blk < (uint64_t)a.num_blocks ? blk : -1;  // corrupt: skip
-  }
+  if (tid < nb) s_tbl[tid] = (uint64_t)(uint32_t)tb < (uint64_t)a.num_blocks ? tb : -1;  // corrupt: skip
   __syncthreads();
   int wg_limit = s_limit[0];
 #pragma unroll
   for (int w = 1; w < W; ++w) wg_limit = max(wg_limit, s_limit[w]);
   const int kend = min(c1, wg_limit);
 
-  u32x4_t qb[RB][D / 32];
   int row_end[RB];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    mq_load_q<D>(qb[b], a.q + ((int64_t)s[b] * a.num_q_heads + h[b]) * D, row_ok[b],
-                 a.scale_log2 < 0.f);
-    // Rows past the batch attend unmasked with q = 0 and are not written.
-    row_end[b] = row_ok[b] ? min(limit[b], c1) : kend;
-  }
+  for (int b = 0; b < RB; ++b)           // rows past the batch attend unmasked with q = 0
+    row_end[b] = row_ok[b] ? min(limit[b], c1) : kend;   // and are not written
   MqState<D, RB> st;
   st.init();
   auto blk_of = [&](int t) -> int { return s_tbl[(t >> lbs) - b0]; };

@@ -15,7 +15,7 @@ namespace {
 constexpr int kAutoMinPartition = 256;       // partition sizes an automatic choice may use
 constexpr int kAutoMaxPartition = 4096;
 constexpr int kAutoBalancedPartition = 1024;  // cap when the batch alone fills the chip
-constexpr int kAutoBalancedPartitionWide = 2048;  // the same cap for 2-byte rows and long tails
+constexpr int kAutoBalancedPartitionWide = 1792;  // the same cap for 2-byte rows and long tails
 constexpr int kAutoBalancedPartitionFp8 = 1536;   // the same cap for FP8 rows and long tails
 constexpr int kFallbackCUs = 256;             // if the device cannot be queried
 constexpr int kMaxDevices = 64;
@@ -147,12 +147,14 @@ void clear_sched(pa::DecodeParams& a) {
 // largest power of two in [256, 4096] that still yields about four
 // work-groups per compute unit; once the (sequence, kv head) pairs alone give
 // that many, partitions only trim the tail left by the longest sequences and
-// are held at 1024 tokens -- 2048 for 2-byte rows and 1536 for FP8 rows when
-// that still splits the longest context (the lognormal GQA batch: 275
-// against 283 us at 2048; its FP8 form 177-180 against 186-188 us at 1536,
-// and 193 at 2048). A split that would cut no more than a short tail off the
-// longest sequence is not worth its combine. The thresholds come from
-// sweeps of 128..4096-token partitions over the decode workloads.
+// are held at 1024 tokens -- 1792 for 2-byte rows and 1536 for FP8 rows when
+// that still splits the longest context (the lognormal GQA batch on the
+// matrix-core item: 262-263 us at 1792 against 264-265 at 1664, 265-266 at
+// 1920, 269-270 at 2048 and 267 at 2304; its FP8 form 156-157 us at 1536,
+// 158 at 1792 and 2560, 161-163 at 3072). A split that would cut no more
+// than a short tail off the longest sequence is not worth its combine. The
+// thresholds come from sweeps of 128..4096-token partitions over the decode
+// workloads.
 int auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int cus,
                    int kv_elem_bytes) {
   const int64_t items = (int64_t)num_seqs * num_kv_heads;

@@ -156,10 +156,11 @@ def test_slot_mapping_validation(lib, args, code):
 @pytest.mark.parametrize("B,Hkv,maxlen,esz,cus,expect", [
     (64, 32, 2046, 2, 256, 1024),  # MHA batch: enough pairs, split held at 1024 tokens
     (64, 32, 2046, 1, 256, 1024),  # its FP8 form
-    (256, 8, 4096, 2, 256, 2048),  # GQA batch, 2-byte rows, lognormal tail past 3072 tokens
+    (256, 8, 4096, 2, 256, 1792),  # GQA batch, 2-byte rows, lognormal tail past 2688 tokens
     (256, 8, 4096, 1, 256, 1536),  # its FP8 form: 1536
     (256, 8, 2304, 1, 256, 1024),  # FP8, 1536 would not split the longest context
-    (256, 8, 3072, 2, 256, 1024),  # 2048 would not split the longest context
+    (256, 8, 2688, 2, 256, 1024),  # 1792 would not split the longest context
+    (256, 8, 2704, 2, 256, 1792),  # one block past it does
     (128, 8, 1536, 2, 256, -1),    # longest context within 1.5 partitions: single pass
     (4, 8, 93064, 2, 256, 2048),   # long contexts: largest split with >= 4 WGs per CU
     (4, 8, 93064, 1, 256, 2048),

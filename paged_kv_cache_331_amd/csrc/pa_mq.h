@@ -307,11 +307,21 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   // Step at t0 into LDS buffer buf; positions >= kend and skipped blocks
   // read the zero chunk (blk_of is only asked for positions in [c0, kend)).
   // A slice's block and the slot of its first row are wave-uniform.
-  auto issue = [&](int t0, int buf) {
+  // The slices' block ids of the step at t0, read one step before its
+  // loads are issued, so that the table read's latency hides behind a
+  // step's products instead of delaying the issue.
+  auto lookup = [&](int t0, int (&ids)[SPW]) {
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
       const int tf = t0 + (64 * (wave + W * u)) / CH;      // the slice's first position
-      const int blk = __builtin_amdgcn_readfirstlane(tf < kend ? blk_of(tf) : -1);
+      ids[u] = tf < kend ? blk_of(tf) : -1;
+    }
+  };
+  auto issue = [&](int t0, int buf, const int (&ids)[SPW]) {
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int tf = t0 + (64 * (wave + W * u)) / CH;      // the slice's first position
+      const int blk = __builtin_amdgcn_readfirstlane(ids[u]);
       const bool ok = blk >= 0 && t0 + dr[u] < kend;
       const uint64_t base = (uint64_t)(uint32_t)(blk * bs + (tf & (bs - 1))) * stride32;
       const uint32_t dst = (uint32_t)(wave + W * u) * 1024 + (uint32_t)buf * TILE;
@@ -424,8 +434,13 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   // loads in flight is the same at every step.
   constexpr bool kIssueFirst = RD == 1;
   const int nsteps = kend > c0 ? (kend - c0 + kMqStep - 1) / kMqStep : 0;
+  int ids[SPW];
 #pragma unroll
-  for (int r = 0; r < RD; ++r) issue(c0 + r * kMqStep, r);
+  for (int r = 0; r < RD; ++r) {
+    lookup(c0 + r * kMqStep, ids);
+    issue(c0 + r * kMqStep, r, ids);
+  }
+  lookup(c0 + RD * kMqStep, ids);
   for (int i = 0; i < nsteps; i += NB) {
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
@@ -433,9 +448,15 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
       if (step >= nsteps) break;                  // uniform
       mq_wait_loads<(RD - 1) * DPS>();            // this wave's loads of this step
       __syncthreads();                            // everyone's
-      if (kIssueFirst) issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
+      if (kIssueFirst) {
+        issue(c0 + (step + RD) * kMqStep, (r + RD) % NB, ids);
+        lookup(c0 + (step + RD + 1) * kMqStep, ids);
+      }
       compute(c0 + step * kMqStep, r);
-      if (!kIssueFirst) issue(c0 + (step + RD) * kMqStep, (r + RD) % NB);
+      if (!kIssueFirst) {
+        issue(c0 + (step + RD) * kMqStep, (r + RD) % NB, ids);
+        lookup(c0 + (step + RD + 1) * kMqStep, ids);
+      }
     }
   }
   mq_wait_loads<0>();

@@ -386,9 +386,16 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
           for (int i = 1; i < 8; ++i) mx = fmaxf(mx, c[b][i / 4][i % 4]);
           mx *= sl2;
         }
-        mx = mq_max_over_groups(mx);
+        // The reference moves only for a row with a key above it by more
+        // than the slack. When no lane of the wave holds such a key (every
+        // step after the first few), the row max across the lane groups is
+        // not needed and the reference stays.
         m_old[b] = st.m[b];
-        const float mn = mx > st.m[b] + kMqSlack ? mx : st.m[b];
+        float mn = st.m[b];
+        if (__ballot(mx > st.m[b] + kMqSlack) != 0) {   // uniform
+          mx = mq_max_over_groups(mx);
+          mn = mx > st.m[b] + kMqSlack ? mx : st.m[b];
+        }
         moved |= mn != m_old[b];
         float p[8];
 #pragma unroll

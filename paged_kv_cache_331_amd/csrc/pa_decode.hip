@@ -901,10 +901,14 @@ __device__ __forceinline__ void decode_item_mma(const DecodeParams& a, int g, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[i] = ts + 4 * gq + i < tend && !bad ? c[i] * sl2 : -INFINITY;
     float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    mx = mq_max_over_groups(mx);
-    const bool up = mx > m + kSlack;
-    const float mn = up ? mx : m;
-    if (__ballot(up) != 0) {                   // uniform: some head moved its reference
+    // A column's reference moves only for a key above it by more than the
+    // slack; unless some lane holds one, the column max across the lane
+    // groups is not needed. When one does, its column moves, so the
+    // accumulators are rescaled in the same branch.
+    float mn = m;
+    if (__ballot(mx > m + kSlack) != 0) {      // uniform
+      mx = mq_max_over_groups(mx);
+      mn = mx > m + kSlack ? mx : m;
       const float alpha = fast_exp2(m - mn);   // 1 where this column did not move
       lsum *= alpha;
 #pragma unroll

@@ -176,7 +176,7 @@ def host_cpus() -> int:
 
 def cpu_workers() -> int:
     """Worker processes for the oracle: every CPU this process may run on,
-    at most 16 (one GPU's share of a GPU machine's host)."""
+    at most 16 (the host cores that go with one GPU on an 8-GPU node)."""
     return max(1, min(host_cpus(), 16))
 
 

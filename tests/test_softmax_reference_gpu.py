@@ -6,18 +6,21 @@ exceeds it by more than a slack, and the max across a row's lane groups is
 reduced only on steps where some lane holds such a key. Two input shapes
 exercise that logic across the whole sequence instead of only its first steps:
 
-* ``ramp``: every K row at position p is 0.02 * p in every element and the
-  queries are positive multiples of the all-ones vector, so the logits rise by
-  about 0.3 (base 2) per key and the reference moves on every step;
+* ``ramp``: every K row at position p is 0.02 * p in every element (0.003 * p
+  over an FP8 cache, whose codes reach 14 at its scale) and the queries are
+  positive multiples of the all-ones vector (8 times larger over FP8), so the
+  logits rise by 0.3-0.6 (base 2) per key and the reference moves on almost
+  every step;
 * ``spike``: seeded K and q, except one position late in each sequence (past
   any shared prefix) whose K row is scaled by 40, so that for some heads one
   key dominates after most of the keys have been seen.
 
 Prefill (the matrix-core core), decode with one and with four query heads per
-kv head (the VALU item, the matrix-core item), with and without a split, and
-the cascade (prefix work-groups, suffix items, combine) are compared with the
-fp64 oracle. Outputs reach single V rows here, so each is held to the decode
-tolerance plus half an ulp of the output type at |ref|.
+kv head (the VALU item, the matrix-core item) over 2-byte and FP8 caches, with
+and without a split, and the cascade (prefix work-groups, suffix items,
+combine) are compared with the fp64 oracle. Outputs reach single V rows here,
+so each is held to the decode tolerance plus half an ulp of the output type
+at |ref|.
 """
 import numpy as np
 import pytest
@@ -26,12 +29,15 @@ import torch
 import oracle
 from paged_kv_cache_331_amd import pa, workloads as wl
 
-from _paged import Device, excess_err, gpu_step, max_err, oracle_caches, say, up16, up32
+from _paged import (Device, excess_err, gpu_step, max_err, oracle_caches, oracle_decode, say,
+                    up16, up32)
 
 pytestmark = pytest.mark.gpu
 
-RAMP_SLOPE = 0.02
+RAMP_SLOPE = {"2byte": 0.02, "fp8": 0.003}
+RAMP_Q = {"2byte": 1.0, "fp8": 8.0}
 SPIKE = 40.0
+E4M3_MAX = 448.0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -58,30 +64,49 @@ def _key_slots(b, s, prefill):
             yield p, "pool", (int(b.block_tables[s, p // bs]), p % bs)
 
 
+def _fp8(b):
+    return getattr(b, "cache_dtype", b.dtype) == "fp8"
+
+
+def _e4m3_codes(x, scale):
+    """E4M3 codes of x / scale (clipped to the format's range), with torch's
+    float8_e4m3fn conversion, as the workload generator makes its pools."""
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.float32(scale), -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def _key_row(b, kind, idx):
-    bits = b.k_new[idx] if kind == "new" else b.key_cache[idx[0], idx[1]]
-    return oracle.to_float64(bits, b.dtype).astype(np.float32)
+    """A K row as the attention reads it (FP8 pool rows scaled by k_scale)."""
+    if kind == "new":
+        return oracle.to_float64(b.k_new[idx], b.dtype).astype(np.float32)
+    row = b.key_cache[idx[0], idx[1]]
+    if _fp8(b):
+        return (oracle.to_float64(row, "fp8") * float(b.k_scale)).astype(np.float32)
+    return oracle.to_float64(row, b.dtype).astype(np.float32)
 
 
 def _set_key_row(b, kind, idx, row):
-    bits = wl.round_to_storage(row, b.dtype)
-    if kind == "new":
-        b.k_new[idx] = bits
+    if kind == "new":                            # the 2-byte row the write stores
+        b.k_new[idx] = wl.round_to_storage(row, b.dtype)
+    elif _fp8(b):
+        b.key_cache[idx[0], idx[1]] = _e4m3_codes(row, b.k_scale)
     else:
-        b.key_cache[idx[0], idx[1]] = bits
+        b.key_cache[idx[0], idx[1]] = wl.round_to_storage(row, b.dtype)
 
 
 def shape_inputs(b, mode, prefill, prefix_len=0):
     """Rewrite the batch's K rows (and, for the ramp, q) in place."""
     Hkv, D = b.spec.num_kv_heads, b.spec.head_size
     if mode == "ramp":
+        kind_ = "fp8" if _fp8(b) else "2byte"
         Hq = b.spec.num_q_heads
-        w = (1.0 + 0.5 * np.arange(Hq, dtype=np.float32) / Hq)[:, None]
+        w = RAMP_Q[kind_] * (1.0 + 0.5 * np.arange(Hq, dtype=np.float32) / Hq)[:, None]
         q = np.broadcast_to(w * np.ones(D, dtype=np.float32), b.q.shape).copy()
         b.q[...] = wl.round_to_storage(q, b.dtype)
         for s in range(b.num_seqs):
             for p, kind, idx in _key_slots(b, s, prefill):
-                _set_key_row(b, kind, idx, np.full((Hkv, D), RAMP_SLOPE * p, dtype=np.float32))
+                _set_key_row(b, kind, idx,
+                             np.full((Hkv, D), RAMP_SLOPE[kind_] * p, dtype=np.float32))
         return
     assert mode == "spike"
     for s in range(b.num_seqs):
@@ -133,7 +158,7 @@ def test_prefill_moving_reference(mode, name, ctx, new):
 
 @pytest.mark.parametrize("mode", ["ramp", "spike"])
 @pytest.mark.parametrize("P", [0, 64])
-@pytest.mark.parametrize("name,nseq", [("llama2_7b_mha", 6), ("gqa_8b", 12)])
+@pytest.mark.parametrize("name,nseq", [("llama2_7b_mha", 6), ("gqa_8b", 12), ("gqa_8b_fp8", 12)])
 def test_decode_moving_reference(mode, P, name, nseq):
     b = wl.make_batch(wl.small_variant(name, nseq))
     shape_inputs(b, mode, prefill=False)
@@ -141,7 +166,7 @@ def test_decode_moving_reference(mode, P, name, nseq):
     d = Device(b)
     _, out = gpu_step(b, d, write=b.spec.cache_write, partition_size=P)
     kc, vc, _ = oracle_caches(b, b.spec.cache_write)
-    ref = oracle.decode(b.q, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype)
+    ref = oracle_decode(b, kc, vc)
     _check(out, ref, b.dtype, "decode")
 
 

@@ -636,10 +636,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& a, int g, int s,
 //   S^T (16 positions x 16 heads)  = K (16 x 128) . Q^T (128 x 16)     (v_mfma_f32_16x16x32)
 //   O^T (16 dims x 16 heads)      += V^T (16 x 16) . P^T (16 x 16)     (v_mfma_f32_16x16x16, per dimension tile)
 // A wave takes 16-position steps of the item in turn. Each step's K and V
-// rows (16 rows of 128 elements each) go from global memory straight into a
-// per-wave LDS ring (global_load_lds_dwordx4 with the non-temporal hint)
-// MmaRows::kRing steps ahead, so a wave only waits on its own loads. The
-// operands are read as:
+// rows (16 rows of 128 elements each) go from global memory straight into
+// the wave's own LDS buffers (global_load_lds_dwordx4 with the non-temporal
+// hint), MmaRows::kRing steps ahead, so a wave only waits on its own loads
+// (with no step ahead, K is waited for first and V lands while the logits
+// and weights are computed). The operands are read as:
 //   * K as the A operand: lane l holds position l % 16 and elements
 //     32 ks + 8 (l / 16) .. + 7 of slice ks;
 //   * V^T as the A operand through the transposing LDS reads, which hand
@@ -734,7 +735,7 @@ template <class QT> struct MmaRows<QT, Fp8> {
 // gets dimension 16 dt + j of its four positions.
 template <class QT> struct MmaRows<QT, QT> {
   static constexpr int kRowBytes = 256;
-  static constexpr int kRing = 1;
+  static constexpr int kRing = 0;                // K first, V behind the logits
   static constexpr int kVReads = 8;
   static constexpr int kAppLanes = 16;
   static __device__ __forceinline__ int key(int T) { return ((T & 7) << 1) | ((T >> 3) & 1); }

@@ -13,8 +13,8 @@
 // tokens' G query heads of kv head g, so each K/V row staged serves every
 // row, on the matrix-core core of pa_mq.h. The work-group walks positions 0 .. (its last token's position)
 // in chunks of 256 table entries staged in LDS; each row masks the keys past
-// its own position. Tiles with more keys (later in a sequence) are
-// dispatched first.
+// its own position. Work items with more keys are dispatched first (see
+// the dispatch order below).
 #include "pa_launch.h"
 #include "pa_mq.h"
 
@@ -37,6 +37,27 @@ template <int D> struct PrefillWaves { static constexpr int value = D == 128 ? P
 template <int D>
 constexpr int prefill_rows_per_wg() {
   return PrefillWaves<D>::value * kMqRowsPerBlock * kPrefillRowBlocks;
+}
+
+// Dispatch order. A work item (sequence s, tile qt) walks c + min(n, (qt + 1)
+// TPW) keys, c being the positions cached before its n new tokens, so in a
+// chunked prefill the tiles of sequences with long contexts are the longest
+// whatever their qt. Each work-group therefore ranks the items by that key
+// count (descending, ties by sequence) and takes the item of its own rank;
+// the count of items ahead of one is a sum over sequences, since a
+// sequence's tiles have the key counts c + TPW, c + 2 TPW, ..., c + n. The
+// ranking costs each work-group (items / threads) x sequences steps, so it
+// is used up to kByKeysMaxSeqs sequences and kByKeysMaxWork items x
+// sequences; beyond that, tiles go by qt, later tiles first (the longest
+// order for whole prompts).
+#ifndef PA_PREFILL_BY_KEYS_MAX_SEQS
+#define PA_PREFILL_BY_KEYS_MAX_SEQS 64
+#endif
+constexpr int kByKeysMaxSeqs = PA_PREFILL_BY_KEYS_MAX_SEQS;
+constexpr int64_t kByKeysMaxWork = 65536;
+__device__ __forceinline__ bool by_keys(int num_seqs, int num_tiles) {
+  return num_seqs <= kByKeysMaxSeqs &&
+         (int64_t)num_seqs * num_seqs * num_tiles <= kByKeysMaxWork;
 }
 
 // Clamped view of sequence s's new-token rows: [a, a + n).
@@ -82,21 +103,60 @@ void prefill_kernel(const PrefillParams p) {
   constexpr int TPW = prefill_rows_per_wg<D>() / G;   // new tokens per work-group
   static_assert(D == 64 || D == 128, "head size");
   __shared__ int32_t s_tbl[kTblChunk];
+  __shared__ int32_t s_seq[3][kByKeysMaxSeqs > 0 ? kByKeysMaxSeqs : 1];   // c, n, a per sequence
+  __shared__ int32_t s_item;
   __shared__ MqLds<D> lds;
 
   const int Hkv = p.num_kv_heads;
-  int wg = blockIdx.x;
-  const int g = wg % Hkv;
-  wg /= Hkv;
-  const int s = wg % p.num_seqs;
-  const int qt = p.num_tiles - 1 - wg / p.num_seqs;   // the longest tiles first
-  int L = p.lens[s];
-  L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
-  int a, n;
-  new_rows(p, s, L, a, n);
-  if (qt * TPW >= n) return;                           // uniform: no token in this tile
-
   const int tid = threadIdx.x;
+  const int g = blockIdx.x % Hkv;
+  const int rank = blockIdx.x / Hkv;
+  int s, qt, L, a, n;
+  if (by_keys(p.num_seqs, p.num_tiles)) {
+    const int S = p.num_seqs;                          // <= kByKeysMaxSeqs
+    for (int i = tid; i < S; i += NT) {
+      int Li = p.lens[i];
+      Li = Li < 0 ? 0 : (Li > p.len_cap ? p.len_cap : Li);
+      int ai, ni;
+      new_rows(p, i, Li, ai, ni);
+      s_seq[0][i] = Li - ni;
+      s_seq[1][i] = ni;
+      s_seq[2][i] = ai;
+    }
+    if (tid == 0) s_item = -1;
+    __syncthreads();
+    for (int idx = tid; idx < S * p.num_tiles; idx += NT) {
+      const int si = idx % S, qi = idx / S;
+      const int ni = s_seq[1][si];
+      if (qi * TPW >= ni) continue;                    // no token in this tile
+      const int x = s_seq[0][si] + min(ni, (qi + 1) * TPW);
+      int ahead = 0;
+      for (int u = 0; u < S; ++u) {
+        const int d = x - s_seq[0][u], nu = s_seq[1][u];
+        // tiles of u with more keys: those from qt = d / TPW on
+        if (d < nu) ahead += (nu + TPW - 1) / TPW - (d < 0 ? 0 : d / TPW);
+        // u's tile with exactly x keys, if any, goes first when u < si
+        if (u < si && d > 0 && d <= nu && (d % TPW == 0 || d == nu)) ++ahead;
+      }
+      if (ahead == rank) s_item = idx;
+    }
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item < 0) return;                              // uniform: ranks past the last item
+    s = item % S;
+    qt = item / S;
+    n = __builtin_amdgcn_readfirstlane(s_seq[1][s]);
+    L = __builtin_amdgcn_readfirstlane(s_seq[0][s]) + n;
+    a = __builtin_amdgcn_readfirstlane(s_seq[2][s]);
+  } else {
+    s = rank % p.num_seqs;
+    qt = p.num_tiles - 1 - rank / p.num_seqs;         // later tiles first
+    L = p.lens[s];
+    L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+    new_rows(p, s, L, a, n);
+    if (qt * TPW >= n) return;                         // uniform: no token in this tile
+  }
+
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 15;

@@ -113,6 +113,47 @@ def test_prefill_scale_sign_zero_and_large(mult):
         assert err <= TOL[b.dtype]
 
 
+@pytest.mark.parametrize("case", ["by_keys", "by_tile"])
+def test_prefill_dispatch_order_every_row_once(case):
+    """Work-groups take their work items in descending order of key count
+    (up to 64 sequences; ties between sequences with equal context and chunk
+    here) or, with more sequences, by query tile. Either way every (token,
+    head) row is computed exactly once: the output starts as NaN and every
+    row is compared with the oracle."""
+    rng = np.random.default_rng([331, 77, 0 if case == "by_keys" else 1])
+    if case == "by_keys":
+        G, S = 4, 24
+        ctx = [int(v) for v in rng.integers(0, 700, S)]
+        new = [int(v) for v in rng.integers(1, 140, S)]
+        ctx[5], new[5] = ctx[2], new[2]                      # equal key counts
+        ctx[9], new[9] = ctx[2] + 32, max(1, new[2] - 32)
+    else:
+        G, S = 1, 65
+        ctx = [int(v) for v in rng.integers(0, 200, S)]
+        new = [int(v) for v in rng.integers(1, 160, S)]
+    spec = wl.PrefillSpec(name=f"pf_order_{case}", num_seqs=S, num_q_heads=2 * G,
+                          num_kv_heads=2, head_size=128, block_size=16,
+                          dtype="bf16" if G > 1 else "fp16", ctx_lo=0, ctx_hi=0, new_lo=1,
+                          new_hi=1, seed_index=700 + G)
+    b = wl.make_prefill_batch(spec, ctx=ctx, new=new)
+    say(f"prefill order {case}: S={S} G={G} T={b.num_tokens}")
+    d = Dev(b)
+    slots = pa.prefill_slot_mapping(d.bt, d.lens, d.qs, b.num_tokens, b.max_query_len,
+                                    spec.block_size, b.max_context_len)
+    pa.cache_write(d.k_new, d.v_new, d.kc, d.vc, slots)
+    out = torch.full_like(d.q, float("nan"))
+    pa.prefill(d.q, d.kc, d.vc, d.bt, d.lens, d.qs, float(b.scale), b.max_query_len,
+               b.max_context_len, out=out)
+    torch.cuda.synchronize()
+    _, kc, vc = _oracle_caches(b)
+    ref = oracle.prefill(b.q, kc, vc, b.block_tables, b.context_lens, b.query_start, b.scale,
+                         b.dtype)
+    assert np.all(np.isfinite(out.float().cpu().numpy()))
+    err = max_err(out, ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[b.dtype]
+
+
 def _edge_spec(bs, D, G, dtype):
     Hkv = 2
     return wl.PrefillSpec(name=f"pf_edge_{bs}_{D}_{G}_{dtype}", num_seqs=4,

@@ -9,12 +9,12 @@
 // positions L - n .. L - 1. The token at position p attends to 0 .. p.
 //
 // Work decomposition: one work-group per (kv head g, sequence s, tile of
-// 128 / G new tokens): its 128 query rows (4 waves x 2 blocks of 16) are those
-// tokens' G query heads of kv head g, so each K/V row staged serves every
-// row, on the matrix-core core of pa_mq.h. The work-group walks positions 0 .. (its last token's position)
-// in chunks of 256 table entries staged in LDS; each row masks the keys past
-// its own position. Work items with more keys are dispatched first (see
-// the dispatch order below).
+// 128 / G new tokens): its 128 query rows (4 waves x 2 blocks of 16) are
+// those tokens' G query heads of kv head g, so each K/V row staged serves
+// every row, on the matrix-core core of pa_mq.h. The work-group walks
+// positions 0 .. (its last token's position) in chunks of 256 table entries
+// staged in LDS; each row masks the keys past its own position. Work items
+// with more keys are dispatched first (see the dispatch order below).
 #include "pa_launch.h"
 #include "pa_mq.h"
 

@@ -114,6 +114,7 @@ void prefill_kernel(const PrefillParams p) {
   int s, qt, L, a, n;
   if (by_keys(p.num_seqs, p.num_tiles)) {
     const int S = p.num_seqs;                          // <= kByKeysMaxSeqs
+    int cached = 0;
     for (int i = tid; i < S; i += NT) {
       int Li = p.lens[i];
       Li = Li < 0 ? 0 : (Li > p.len_cap ? p.len_cap : Li);
@@ -122,30 +123,38 @@ void prefill_kernel(const PrefillParams p) {
       s_seq[0][i] = Li - ni;
       s_seq[1][i] = ni;
       s_seq[2][i] = ai;
+      cached |= Li > ni;
     }
-    if (tid == 0) s_item = -1;
-    __syncthreads();
-    for (int idx = tid; idx < S * p.num_tiles; idx += NT) {
-      const int si = idx % S, qi = idx / S;
-      const int ni = s_seq[1][si];
-      if (qi * TPW >= ni) continue;                    // no token in this tile
-      const int x = s_seq[0][si] + min(ni, (qi + 1) * TPW);
-      int ahead = 0;
-      for (int u = 0; u < S; ++u) {
-        const int d = x - s_seq[0][u], nu = s_seq[1][u];
-        // tiles of u with more keys: those from qt = d / TPW on
-        if (d < nu) ahead += (nu + TPW - 1) / TPW - (d < 0 ? 0 : d / TPW);
-        // u's tile with exactly x keys, if any, goes first when u < si
-        if (u < si && d > 0 && d <= nu && (d % TPW == 0 || d == nu)) ++ahead;
+    if (tid == 0) s_item = rank < S * p.num_tiles ? rank % S + S * (p.num_tiles - 1 - rank / S) : -1;
+    // Whole prompts only (no cached positions): the tile order, later tiles
+    // first, is the order by key count but for each sequence's last, partial
+    // tile, so the ranking is skipped.
+    if (__syncthreads_or(cached)) {
+      if (tid == 0) s_item = -1;
+      __syncthreads();
+      for (int idx = tid; idx < S * p.num_tiles; idx += NT) {
+        const int si = idx % S, qi = idx / S;
+        const int ni = s_seq[1][si];
+        if (qi * TPW >= ni) continue;                  // no token in this tile
+        const int x = s_seq[0][si] + min(ni, (qi + 1) * TPW);
+        int ahead = 0;
+        for (int u = 0; u < S; ++u) {
+          const int d = x - s_seq[0][u], nu = s_seq[1][u];
+          // tiles of u with more keys: those from qt = d / TPW on
+          if (d < nu) ahead += (nu + TPW - 1) / TPW - (d < 0 ? 0 : d / TPW);
+          // u's tile with exactly x keys, if any, goes first when u < si
+          if (u < si && d > 0 && d <= nu && (d % TPW == 0 || d == nu)) ++ahead;
+        }
+        if (ahead == rank) s_item = idx;
       }
-      if (ahead == rank) s_item = idx;
+      __syncthreads();
     }
-    __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item < 0) return;                              // uniform: ranks past the last item
     s = item % S;
     qt = item / S;
     n = __builtin_amdgcn_readfirstlane(s_seq[1][s]);
+    if (qt * TPW >= n) return;                         // uniform: no token in this tile
     L = __builtin_amdgcn_readfirstlane(s_seq[0][s]) + n;
     a = __builtin_amdgcn_readfirstlane(s_seq[2][s]);
   } else {

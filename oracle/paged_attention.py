@@ -295,7 +295,8 @@ def decode_two_level(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarr
 
 def prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             block_tables: np.ndarray, context_lens: np.ndarray, query_start: np.ndarray,
-            scale, dtype: str) -> np.ndarray:
+            scale, dtype: str, cache_dtype: Optional[str] = None, k_scale: float = 1.0,
+            v_scale: float = 1.0) -> np.ndarray:
     """Causal attention of each sequence's new tokens over its paged cache.
 
     The book's §4 prefill phase: the N new tokens' K and V are first written
@@ -305,6 +306,9 @@ def prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
     ``query_start[s] .. query_start[s+1]-1`` of ``q``) at positions
     ``L - n .. L - 1`` of its ``L = context_lens[s]`` cached positions. The
     new token at position ``p`` attends to positions ``0 .. p``.
+    ``cache_dtype`` (default: ``dtype``) is the caches' type, as in
+    :func:`decode`: an FP8 cache's rows are its codes' values times
+    ``k_scale`` / ``v_scale``.
     Returns float64 ``[num_tokens, Hq, D]``.
     """
     T, Hq, D = q.shape
@@ -321,8 +325,8 @@ def prefill(q: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
             continue
         assert n <= L, "more new tokens than cached positions"
         for g in range(Hkv):
-            K = gather_positions(key_cache, block_tables[s], L, g, dtype)
-            V = gather_positions(value_cache, block_tables[s], L, g, dtype)
+            K = gather_positions(key_cache, block_tables[s], L, g, cache_dtype or dtype, k_scale)
+            V = gather_positions(value_cache, block_tables[s], L, g, cache_dtype or dtype, v_scale)
             for i in range(n):
                 pos = L - n + i
                 for h in range(g * G, (g + 1) * G):

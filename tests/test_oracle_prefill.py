@@ -118,3 +118,72 @@ def test_prefill_slots_last_token_is_decode_slot():
     sl = oracle.prefill_slot_mapping(bt, lens, qs, kc.shape[1])
     dec = oracle.slot_mapping(bt, lens, kc.shape[1])
     assert np.array_equal(sl[qs[1:] - 1], dec)
+
+
+def _fp8_case(seed, **kw):
+    """A case whose caches hold E4M3 codes (torch's float8_e4m3fn encoding of
+    N(0, 1) / 2**-4, so codes of every magnitude occur)."""
+    q, kc, vc, bt, lens, qs = _case(seed, **kw)
+    rng = np.random.default_rng([seed, 8])
+    enc = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    kc8 = enc(rng.standard_normal(kc.shape) * 16.0)
+    vc8 = enc(rng.standard_normal(vc.shape) * 16.0)
+    return q, kc8, vc8, bt, lens, qs
+
+
+def _e4m3_torch(codes):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_fp8_cache_matches_bruteforce(seed):
+    """[blog] §4.3 FP8 K/V: the rows attended are the codes' values times the
+    tensor's scale; decoded here by torch, not by the oracle's decoder."""
+    q, kc, vc, bt, lens, qs = _fp8_case(seed, dtype="bf16")
+    scale, ks, vs = np.float32(0.3), 0.0625, 0.03125
+    got = oracle.prefill(q, kc, vc, bt, lens, qs, scale, "bf16", cache_dtype="fp8", k_scale=ks,
+                         v_scale=vs)
+    qf = oracle.to_float64(q, "bf16")
+    kf, vf = _e4m3_torch(kc) * ks, _e4m3_torch(vc) * vs
+    bs = kc.shape[1]
+    Hq, Hkv = q.shape[1], kc.shape[2]
+    for s in range(len(lens)):
+        n = qs[s + 1] - qs[s]
+        for i in range(n):
+            pos = lens[s] - n + i
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                K = np.stack([kf[bt[s, t // bs], t % bs, g] for t in range(pos + 1)])
+                V = np.stack([vf[bt[s, t // bs], t % bs, g] for t in range(pos + 1)])
+                p = scipy.special.softmax(float(scale) * (K @ qf[qs[s] + i, h]))
+                assert np.allclose(got[qs[s] + i, h], p @ V, rtol=0, atol=1e-13)
+
+
+def test_prefill_fp8_rows_equal_fp8_decode_at_their_length():
+    q, kc, vc, bt, lens, qs = _fp8_case(31, B=3, Hq=8, Hkv=2, D=16, dtype="fp16")
+    scale, ks, vs = np.float32(0.25), 0.125, 0.5
+    got = oracle.prefill(q, kc, vc, bt, lens, qs, scale, "fp16", cache_dtype="fp8", k_scale=ks,
+                         v_scale=vs)
+    for s in range(3):
+        n = qs[s + 1] - qs[s]
+        for i in range(n):
+            L1 = np.array([lens[s] - n + i + 1], np.int32)
+            ref = oracle.decode(q[qs[s] + i][None], kc, vc, bt[s:s + 1], L1, scale, "fp16",
+                                cache_dtype="fp8", k_scale=ks, v_scale=vs)
+            assert np.max(np.abs(got[qs[s] + i] - ref[0])) <= 1e-13
+
+
+def test_prefill_fp8_scales_fold_into_logits_and_output():
+    """k_scale multiplies every logit (so it trades with the attention scale)
+    and v_scale every output; a dropped or swapped scale fails one of these."""
+    q, kc, vc, bt, lens, qs = _fp8_case(41, dtype="fp16")
+    base = oracle.prefill(q, kc, vc, bt, lens, qs, np.float32(0.5), "fp16", cache_dtype="fp8",
+                          k_scale=0.25, v_scale=1.0)
+    folded = oracle.prefill(q, kc, vc, bt, lens, qs, np.float32(0.125), "fp16",
+                            cache_dtype="fp8", k_scale=1.0, v_scale=1.0)
+    assert np.allclose(base, folded, rtol=0, atol=1e-13)
+    scaled = oracle.prefill(q, kc, vc, bt, lens, qs, np.float32(0.5), "fp16", cache_dtype="fp8",
+                            k_scale=0.25, v_scale=4.0)
+    assert np.allclose(scaled, 4.0 * base, rtol=0, atol=1e-12)
+    assert np.max(np.abs(scaled - base)) > 1e-3

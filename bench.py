@@ -336,7 +336,8 @@ def prefill_cpu_baseline(batch, budget_s: float) -> dict:
         n = int(qs[s + 1] - qs[s])
         L1 = np.array([int(b.context_lens[s]) - n + i + 1], np.int32)
         oracle.decode(b.q[qs[s] + i][None], b.key_cache, b.value_cache,
-                      b.block_tables[s:s + 1], L1, b.scale, b.dtype)
+                      b.block_tables[s:s + 1], L1, b.scale, b.dtype,
+                      cache_dtype=b.cache_dtype, k_scale=b.k_scale, v_scale=b.v_scale)
 
     n = cpu_workers()
     rate, done, dt = run_oracle_timed(one, len(rows), budget_s, n)
@@ -369,7 +370,13 @@ def run_prefill(args) -> int:
     pa.load()          # the HIP library must be built; there is no fallback
     tdt = torch.float16 if spec.dtype == "fp16" else torch.bfloat16
     up = lambda a: torch.from_numpy(a.view(np.int16)).view(tdt).cuda()
-    q, kc, vc, k_new, v_new = up(b.q), up(b.key_cache), up(b.value_cache), up(b.k_new), up(b.v_new)
+    fp8 = b.cache_dtype == "fp8"
+    q, k_new, v_new = up(b.q), up(b.k_new), up(b.v_new)
+    if fp8:
+        kc, vc = torch.from_numpy(b.key_cache).cuda(), torch.from_numpy(b.value_cache).cuda()
+    else:
+        kc, vc = up(b.key_cache), up(b.value_cache)
+    ks, vs = float(b.k_scale), float(b.v_scale)
     bt = torch.from_numpy(b.block_tables).cuda()
     lens = torch.from_numpy(b.context_lens).cuda()
     qs = torch.from_numpy(b.query_start).cuda()
@@ -380,10 +387,17 @@ def run_prefill(args) -> int:
 
     def step(ev0=None, ev1=None):
         pa.prefill_slot_mapping(bt, lens, qs, T, mq, spec.block_size, ml, out=slots, stream=stream)
-        pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
+        if fp8:
+            pa.cache_write_fp8(k_new, v_new, kc, vc, slots, ks, vs, stream=stream)
+        else:
+            pa.cache_write(k_new, v_new, kc, vc, slots, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
-        pa.prefill(q, kc, vc, bt, lens, qs, float(b.scale), mq, ml, out=out, stream=stream)
+        if fp8:
+            pa.prefill_fp8(q, kc, vc, bt, lens, qs, float(b.scale), ks, vs, mq, ml, out=out,
+                           stream=stream)
+        else:
+            pa.prefill(q, kc, vc, bt, lens, qs, float(b.scale), mq, ml, out=out, stream=stream)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -413,9 +427,12 @@ def run_prefill(args) -> int:
                    "head_size": spec.head_size, "block_size": spec.block_size,
                    "cached_before": f"uniform [{spec.ctx_lo}, {spec.ctx_hi}]",
                    "new_per_seq": f"uniform [{spec.new_lo}, {spec.new_hi}]",
+                   "cache": (f"fp8 (E4M3), scale {spec.kv_scale}" if fp8 else spec.dtype),
                    "step": "prefill slot mapping + cache write + causal prefill",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "pa_prefill (events around the call on its stream)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("pa_prefill_fp8" if fp8 else "pa_prefill")
+                               + " (events around the call on its stream)",
                      "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": None,
                      "algorithmic_flops_per_launch": flops,

@@ -480,6 +480,27 @@ PA_API int pa_prefill(const void* q, const void* key_cache, const void* value_ca
                       int32_t dtype, void* stream);
 
 /*
+ * pa_prefill_fp8 -- pa_prefill over FP8 (E4M3) caches (the intelliparadigm
+ * article's §4.3: FP8 K/V among the cache precisions).
+ * A code c stands for value(c) * k_scale in key_cache and value(c) * v_scale
+ * in value_cache, the reading pa_decode_fp8 takes; the new tokens are
+ * written with pa_cache_write_fp8. q and out keep the 2-byte type dtype.
+ * Codes are converted exactly to dtype before the products; k_scale joins
+ * the softmax scale and v_scale the output.
+ * caches : uint8 [num_blocks, block_size, num_kv_heads, head_size] (device)
+ * Errors: as pa_prefill, and PA_ERR_SHAPE for a k_scale or v_scale that is
+ * not finite and positive.
+ */
+PA_API int pa_prefill_fp8(const void* q, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* query_start, float scale, float k_scale, float v_scale,
+                          void* out, int32_t num_seqs, int32_t num_tokens,
+                          int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_size, int32_t block_size, int64_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+                          void* stream);
+
+/*
  * Host block pool -- the bookkeeping that produces the tables (host memory
  * only; no device work). A block's reference count says how many tables
  * point at it ("PagedAttention 机制" §5.3.4 BlockAllocator). The free list is

@@ -423,6 +423,66 @@ int cascade_impl(const void* q, const void* key_cache, const void* value_cache,
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// Shared body of pa_prefill and pa_prefill_fp8 (fp8: the caches hold E4M3
+// codes standing for their values times k_scale / v_scale).
+int prefill_call(const void* q, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* context_lens,
+                 const int32_t* query_start, float scale, void* out, int32_t num_seqs,
+                 int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_size, int32_t block_size, int64_t num_blocks,
+                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype, bool fp8,
+                 float k_scale, float v_scale, void* stream) {
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 0 ||
+      max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (fp8 && (!valid_scale(k_scale) || !valid_scale(v_scale))) return PA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  // New tokens were written into the pool, so it has blocks; the matrix-core
+  // kernel also relies on slot 0 existing (a masked position reads it).
+  if (num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
+  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start ||
+      !out)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+    return PA_ERR_UNSUPPORTED;
+  pa::PrefillParams p = {};
+  p.q = (const uint16_t*)q;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.bt = block_tables;
+  p.lens = context_lens;
+  p.query_start = query_start;
+  p.out = (uint16_t*)out;
+  // K's scale multiplies every logit: it joins the softmax scale (a positive
+  // factor, so the sign the kernel folds into q is unchanged).
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634 * (fp8 ? (double)k_scale : 1.0));
+  p.v_scale = fp8 ? v_scale : 1.f;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.max_query_len = max_query_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.log2_block_size = ilog2_exact(block_size);
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.len_cap = max_context_len;
+  p.num_blocks = num_blocks;
+  const hipError_t e = pa::launch_prefill(p, dtype, head_size, group, fp8,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -663,50 +723,23 @@ int pa_prefill(const void* q, const void* key_cache, const void* value_cache,
                int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
                int32_t num_kv_heads, int32_t head_size, int32_t block_size, int64_t num_blocks,
                int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype, void* stream) {
-  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_BF16) return PA_ERR_DTYPE;
-  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
-      num_kv_heads < 1 || head_size < 1 || block_size < 1 || num_blocks < 0 ||
-      max_blocks_per_seq < 1 || max_context_len < 0)
-    return PA_ERR_SHAPE;
-  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  if (max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-  if (!isfinite(scale)) return PA_ERR_SHAPE;
-  const int group = num_q_heads / num_kv_heads;
-  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
-  // New tokens were written into the pool, so it has blocks; the matrix-core
-  // kernel also relies on slot 0 existing (a masked position reads it).
-  if (num_blocks < 1) return PA_ERR_SHAPE;
-  if (num_blocks * (int64_t)block_size > INT32_MAX) return PA_ERR_SHAPE;   // int32 slots
-  if (!q || !key_cache || !value_cache || !block_tables || !context_lens || !query_start ||
-      !out)
-    return PA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
-    return PA_ERR_UNSUPPORTED;
-  pa::PrefillParams p = {};
-  p.q = (const uint16_t*)q;
-  p.kc = key_cache;
-  p.vc = value_cache;
-  p.bt = block_tables;
-  p.lens = context_lens;
-  p.query_start = query_start;
-  p.out = (uint16_t*)out;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  p.num_seqs = num_seqs;
-  p.num_tokens = num_tokens;
-  p.max_query_len = max_query_len;
-  p.num_q_heads = num_q_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.block_size = block_size;
-  p.log2_block_size = ilog2_exact(block_size);
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.len_cap = max_context_len;
-  p.num_blocks = num_blocks;
-  const hipError_t e = pa::launch_prefill(p, dtype, head_size, group, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return prefill_call(q, key_cache, value_cache, block_tables, context_lens, query_start, scale,
+                      out, num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                      dtype, false, 1.f, 1.f, stream);
+}
+
+int pa_prefill_fp8(const void* q, const void* key_cache, const void* value_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, float scale, float k_scale, float v_scale,
+                   void* out, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                   int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                   int32_t max_context_len, int32_t dtype, void* stream) {
+  return prefill_call(q, key_cache, value_cache, block_tables, context_lens, query_start, scale,
+                      out, num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads,
+                      head_size, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                      dtype, true, k_scale, v_scale, stream);
 }
 
 

@@ -96,9 +96,11 @@ struct PrefillParams {
   int32_t num_q_heads, num_kv_heads, block_size, log2_block_size;
   int32_t max_blocks_per_seq, len_cap, num_tiles;
   int64_t num_blocks;
+  float v_scale;              // FP8 cache: V's scale (K's is in scale_log2)
 };
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group,
+// fp8: the caches hold E4M3 codes.
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group, bool fp8,
                           hipStream_t stream);
 hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream);
 

@@ -35,7 +35,10 @@
 // ds_read_b64_tr_b16, which hand each lane one dimension of four keys, 8
 // rows per pass). A wave's load fills 1 KB of a tile, each lane fetching the
 // chunk that lands at its 16 bytes. A position with no slot loads a zero
-// chunk.
+// chunk. An FP8 (E4M3) cache goes through registers instead: each lane
+// fetches its row's codes two steps ahead, converts them exactly to the
+// query's 2-byte type and writes them into the same swizzled layout, so the
+// products read the tiles the same way.
 #pragma once
 
 #include "pa_device.h"
@@ -222,9 +225,9 @@ __device__ __forceinline__ void mq_load_q(u32x4_t (&qb)[D / 32], const uint16_t*
 // before the softmax (32 fewer VGPRs at head size 128, for callers that
 // share a register budget).
 template <class DT, int D, int RB, int W = kMqWaves, int RD = kMqRing, bool LEAN = false,
-          class BlkOf>
+          bool F8 = false, class BlkOf>
 __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb)[RB][D / 32],
-                                          MqLds<D, RD + 1>& lds, const uint16_t* kc, const uint16_t* vc,
+                                          MqLds<D, RD + 1>& lds, const void* kc, const void* vc,
                                           int64_t tok_stride, int g, int c0, int kend,
                                           const int (&row_end)[RB], float sl2, int bs,
                                           BlkOf blk_of) {
@@ -243,8 +246,8 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15;
   const int grp = lane >> 4;
-  const uint16_t* kbase = kc + (int64_t)g * D;
-  const uint16_t* vbase = vc + (int64_t)g * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(kc) + (int64_t)g * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(vc) + (int64_t)g * D;
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kMqZeroChunk);
   const uint32_t stride32 = (uint32_t)tok_stride;   // Hkv * D < 2^31 elements
 
@@ -439,8 +442,77 @@ __device__ __forceinline__ void mq_attend(MqState<D, RB>& st, const u32x4_t (&qb
   // loads overlap step i's products; deeper rings issue it after them.
   // Steps past the range load zeros and are never computed, so the count of
   // loads in flight is the same at every step.
-  constexpr bool kIssueFirst = RD == 1;
   const int nsteps = kend > c0 ? (kend - c0 + kMqStep - 1) / kMqStep : 0;
+  if constexpr (F8) {
+    // FP8 cache: lane rows fr of the step (the wave's RPW rows share a
+    // block), EPT codes each from code fe on, fetched into registers two
+    // steps ahead (register set step % 2) and converted into LDS buffer
+    // step % 2 after the previous step's products. At the barrier of step i
+    // every wave has written step i and finished reading step i - 1, whose
+    // buffer then takes step i + 1.
+    static_assert(RD == 1, "FP8 tiles: two LDS buffers");
+    constexpr int EPT = kMqStep * D / (W * 64);   // codes per lane and tensor
+    static_assert(EPT == 8 || EPT == 16, "FP8 staging layout");
+    constexpr int LPRW = D / EPT;                 // lanes per key row
+    constexpr int RPW = 64 / LPRW;                // key rows per wave
+    typedef uint32_t f8row __attribute__((ext_vector_type(EPT / 4)));
+    const int fr = wave * RPW + lane / LPRW;
+    const int fe = (lane % LPRW) * EPT;
+    const uint8_t* kb8 = static_cast<const uint8_t*>(kc) + (int64_t)g * D + fe;
+    const uint8_t* vb8 = static_cast<const uint8_t*>(vc) + (int64_t)g * D + fe;
+    const uint8_t* zero8 = reinterpret_cast<const uint8_t*>(kMqZeroChunk);
+    // LDS byte addresses (buffer 0) of the lane's 16-byte chunks, swizzled as
+    // the direct loads place them.
+    uint32_t kdst[EPT / 8], vdst[EPT / 8];
+#pragma unroll
+    for (int cc = 0; cc < EPT / 8; ++cc) {
+      const int sc = fe / 8 + cc;
+      kdst[cc] = k0 + (uint32_t)(fr * D + (sc ^ (fr % CH16)) * 8) * 2;
+      vdst[cc] = v0 + (uint32_t)(fr * D + (2 * ((sc >> 1) ^ vsw(fr)) + (sc & 1)) * 8) * 2;
+    }
+    auto fetch = [&](int t0, f8row& kr, f8row& vr) {
+      const int tw = t0 + wave * RPW;              // the wave's first row
+      const int blk = tw < kend ? __builtin_amdgcn_readfirstlane(blk_of(tw)) : -1;
+      const bool ok = blk >= 0 && t0 + fr < kend;
+      const uint64_t off = (uint64_t)(uint32_t)(blk * bs + ((t0 + fr) & (bs - 1))) * stride32;
+      kr = *(const __attribute__((address_space(1))) f8row*)(ok ? kb8 + off : zero8);
+      vr = *(const __attribute__((address_space(1))) f8row*)(ok ? vb8 + off : zero8);
+    };
+    auto land = [&](int buf, const f8row& kr, const f8row& vr) {
+#pragma unroll
+      for (int cc = 0; cc < EPT / 8; ++cc) {
+        const u32x4_t kw = {Fp8Pair<DT>::template get<false>(kr[2 * cc]),
+                            Fp8Pair<DT>::template get<true>(kr[2 * cc]),
+                            Fp8Pair<DT>::template get<false>(kr[2 * cc + 1]),
+                            Fp8Pair<DT>::template get<true>(kr[2 * cc + 1])};
+        const u32x4_t vw = {Fp8Pair<DT>::template get<false>(vr[2 * cc]),
+                            Fp8Pair<DT>::template get<true>(vr[2 * cc]),
+                            Fp8Pair<DT>::template get<false>(vr[2 * cc + 1]),
+                            Fp8Pair<DT>::template get<true>(vr[2 * cc + 1])};
+        *reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(kdst[cc] + (uint32_t)buf * TILE)) = kw;
+        *reinterpret_cast<mq_lds_u32x4*>(mq_lds_ptr(vdst[cc] + (uint32_t)buf * TILE)) = vw;
+      }
+    };
+    f8row kr8[2], vr8[2];
+    if (nsteps > 0) fetch(c0, kr8[0], vr8[0]);
+    if (nsteps > 1) fetch(c0 + kMqStep, kr8[1], vr8[1]);
+    if (nsteps > 0) land(0, kr8[0], vr8[0]);
+    if (nsteps > 2) fetch(c0 + 2 * kMqStep, kr8[0], vr8[0]);
+    for (int i = 0; i < nsteps; i += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int step = i + r;
+        if (step >= nsteps) break;                // uniform
+        __syncthreads();
+        compute(c0 + step * kMqStep, r);
+        if (step + 1 < nsteps) land(1 - r, kr8[1 - r], vr8[1 - r]);
+        if (step + 3 < nsteps) fetch(c0 + (step + 3) * kMqStep, kr8[1 - r], vr8[1 - r]);
+      }
+    }
+    __syncthreads();   // every read is done: LDS is free
+    return;
+  }
+  constexpr bool kIssueFirst = RD == 1;
   int ids[SPW];
 #pragma unroll
   for (int r = 0; r < RD; ++r) {

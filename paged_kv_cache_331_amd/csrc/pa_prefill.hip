@@ -87,14 +87,15 @@ __global__ __launch_bounds__(kSlotThreads) void prefill_slot_kernel(const Prefil
 // fragments read just before their products) and a register cap that spills
 // a few values: chunked GQA prefill 177-179 against 184-188 us. One query
 // head per kv head keeps two per CU (the same form measured 93-95 against
-// 92-93 us on the MHA prompts).
-template <int G> struct PrefillOccupancy {
+// 92-93 us on the MHA prompts). Over an FP8 cache the codes staged in
+// registers take the room of the third work-group: two per CU.
+template <int G, bool F8> struct PrefillOccupancy {
   static constexpr bool kLean = G >= 4;
-  static constexpr int kWavesPerEu = G >= 4 ? 3 : 1;   // 1: no bound (two fit)
+  static constexpr int kWavesPerEu = G >= 4 && !F8 ? 3 : 1;   // 1: no bound (two fit)
 };
 
-template <class DT, int D, int G>
-__global__ __launch_bounds__(PrefillWaves<D>::value * 64, PrefillOccupancy<G>::kWavesPerEu)
+template <class DT, int D, int G, bool F8>
+__global__ __launch_bounds__(PrefillWaves<D>::value * 64, (PrefillOccupancy<G, F8>::kWavesPerEu))
 void prefill_kernel(const PrefillParams p) {
   using S = Storage<DT>;
   constexpr int W = PrefillWaves<D>::value;
@@ -105,7 +106,7 @@ void prefill_kernel(const PrefillParams p) {
   __shared__ int32_t s_tbl[kTblChunk];
   __shared__ int32_t s_seq[3][kByKeysMaxSeqs > 0 ? kByKeysMaxSeqs : 1];   // c, n, a per sequence
   __shared__ int32_t s_item;
-  __shared__ MqLds<D> lds;
+  __shared__ MqLds<D, F8 ? 2 : kMqBufs> lds;
 
   const int Hkv = p.num_kv_heads;
   const int tid = threadIdx.x;
@@ -206,16 +207,16 @@ void prefill_kernel(const PrefillParams p) {
     }
     __syncthreads();
     auto blk_of = [&](int t) -> int { return s_tbl[(t >> lbs) - b0]; };
-    mq_attend<DT, D, RB, W, kMqRing, PrefillOccupancy<G>::kLean>(st, qb, lds, static_cast<const uint16_t*>(p.kc),
-                         static_cast<const uint16_t*>(p.vc), tok_stride, g, c0, c1, row_end,
-                         fabsf(p.scale_log2), bs, blk_of);   // ends with a barrier: s_tbl is free again
+    mq_attend<DT, D, RB, W, F8 ? 1 : kMqRing, PrefillOccupancy<G, F8>::kLean, F8>(
+        st, qb, lds, p.kc, p.vc, tok_stride, g, c0, c1, row_end, fabsf(p.scale_log2), bs,
+        blk_of);   // ends with a barrier: s_tbl is free again
   }
 
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const float lsum = mq_sum_over_groups(st.lsum[b]);
     if (!row_ok[b]) continue;
-    const float inv = 1.f / lsum;
+    const float inv = F8 ? p.v_scale / lsum : 1.f / lsum;
     uint16_t* o = p.out + ((int64_t)(a + ti[b]) * p.num_q_heads + h[b]) * D + 4 * grp;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -229,7 +230,7 @@ void prefill_kernel(const PrefillParams p) {
   }
 }
 
-template <class DT, int D, int G>
+template <class DT, int D, int G, bool F8>
 hipError_t launch_pf(const PrefillParams& p, hipStream_t st) {
   constexpr int TPW = prefill_rows_per_wg<D>() / G;
   PrefillParams q = p;
@@ -237,38 +238,41 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t st) {
   const uint64_t nwg = (uint64_t)p.num_kv_heads * p.num_seqs * q.num_tiles;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7fffffffull) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G>), dim3((uint32_t)nwg),
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G, F8>), dim3((uint32_t)nwg),
                      dim3(PrefillWaves<D>::value * 64), 0, st,
                      q);
   return hipGetLastError();
 }
 
-template <class DT, int D>
+template <class DT, int D, bool F8>
 hipError_t launch_pf_g(const PrefillParams& p, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_pf<DT, D, 1>(p, st);
-    case 2: return launch_pf<DT, D, 2>(p, st);
-    case 4: return launch_pf<DT, D, 4>(p, st);
-    case 8: return launch_pf<DT, D, 8>(p, st);
+    case 1: return launch_pf<DT, D, 1, F8>(p, st);
+    case 2: return launch_pf<DT, D, 2, F8>(p, st);
+    case 4: return launch_pf<DT, D, 4, F8>(p, st);
+    case 8: return launch_pf<DT, D, 8, F8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <class DT>
+template <class DT, bool F8>
 hipError_t launch_pf_d(const PrefillParams& p, int head_size, int group, hipStream_t st) {
   switch (head_size) {
-    case 64: return launch_pf_g<DT, 64>(p, group, st);
-    case 128: return launch_pf_g<DT, 128>(p, group, st);
+    case 64: return launch_pf_g<DT, 64, F8>(p, group, st);
+    case 128: return launch_pf_g<DT, 128, F8>(p, group, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group,
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int group, bool fp8,
                           hipStream_t stream) {
-  return dtype == 0 ? launch_pf_d<Fp16>(p, head_size, group, stream)
-                    : launch_pf_d<Bf16>(p, head_size, group, stream);
+  if (fp8)
+    return dtype == 0 ? launch_pf_d<Fp16, true>(p, head_size, group, stream)
+                      : launch_pf_d<Bf16, true>(p, head_size, group, stream);
+  return dtype == 0 ? launch_pf_d<Fp16, false>(p, head_size, group, stream)
+                    : launch_pf_d<Bf16, false>(p, head_size, group, stream);
 }
 
 hipError_t launch_prefill_slots(const PrefillParams& p, hipStream_t stream) {

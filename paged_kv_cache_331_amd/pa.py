@@ -47,6 +47,9 @@ SIGNATURES = {
                                                _i32, _vp, _vp]),
     "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp]),
+    "pa_prefill_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                      _vp]),
     "pa_pool_create": (_vp, [_i32]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_num_free": (_i32, [_vp]),
@@ -412,6 +415,29 @@ def prefill(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                            bs, NB, MB, int(max_context_len), dtype_code(q.dtype),
                            _stream(stream))
     _check("pa_prefill", st)
+    return out
+
+
+def prefill_fp8(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                query_start: torch.Tensor, scale: float, k_scale: float, v_scale: float,
+                max_query_len: int, max_context_len: int, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """prefill over uint8 E4M3 caches whose codes stand for value * k_scale / v_scale."""
+    T, Hq, D = q.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    B, MB = block_tables.shape
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().pa_prefill_fp8(_dev(q, "q"), _dev(key_cache, "key_cache"),
+                               _dev(value_cache, "value_cache"),
+                               _dev(block_tables, "block_tables"),
+                               _dev(context_lens, "context_lens"),
+                               _dev(query_start, "query_start"), float(scale), float(k_scale),
+                               float(v_scale), _dev(out, "out"), B, T, int(max_query_len), Hq,
+                               Hkv, D, bs, NB, MB, int(max_context_len), dtype_code(q.dtype),
+                               _stream(stream))
+    _check("pa_prefill_fp8", st)
     return out
 
 

@@ -143,6 +143,8 @@ class PrefillSpec:
     new_lo: int
     new_hi: int
     seed_index: int
+    cache_dtype: str = ""              # "" = dtype; "fp8" = E4M3 codes with kv_scale
+    kv_scale: float = 2.0 ** -5        # fp32 scale of both FP8 cache tensors
 
     @property
     def group_size(self) -> int:
@@ -160,7 +162,15 @@ PREFILL_CONFIGS = {
         head_size=128, block_size=16, dtype="bf16", ctx_lo=0, ctx_hi=2048, new_lo=64, new_hi=512,
         seed_index=9),
 }
+# The same batches over FP8 (E4M3) caches: the same lengths (same seed),
+# pools of E4M3 codes of N(0,1) / kv_scale as in the FP8 decode batches.
+PREFILL_CONFIGS["llama2_7b_prefill_fp8"] = replace(PREFILL_CONFIGS["llama2_7b_prefill"],
+                                                   name="llama2_7b_prefill_fp8", cache_dtype="fp8")
+PREFILL_CONFIGS["gqa_8b_chunked_prefill_fp8"] = replace(
+    PREFILL_CONFIGS["gqa_8b_chunked_prefill"], name="gqa_8b_chunked_prefill_fp8",
+    cache_dtype="fp8")
 PREFILL_ORDER = ("llama2_7b_prefill", "gqa_8b_chunked_prefill")
+PREFILL_FP8_ORDER = ("llama2_7b_prefill_fp8", "gqa_8b_chunked_prefill_fp8")
 
 
 @dataclass
@@ -184,6 +194,18 @@ class PrefillBatch:
     @property
     def dtype(self) -> str:
         return self.spec.dtype
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.spec.cache_dtype or self.spec.dtype
+
+    @property
+    def k_scale(self) -> np.float32:
+        return np.float32(self.spec.kv_scale if self.cache_dtype == "fp8" else 1.0)
+
+    @property
+    def v_scale(self) -> np.float32:
+        return self.k_scale
 
     @property
     def num_seqs(self) -> int:
@@ -472,7 +494,8 @@ def make_prefill_batch(spec: PrefillSpec, *, ctx: Optional[Sequence[int]] = None
                        num_kv_heads=spec.num_kv_heads, head_size=spec.head_size,
                        block_size=spec.block_size, dtype=spec.dtype, lengths="uniform",
                        len_lo=1, len_hi=max(1, int(lens.max()) if lens.size else 1),
-                       seed_index=spec.seed_index)
+                       seed_index=spec.seed_index, cache_dtype=spec.cache_dtype,
+                       kv_scale=spec.kv_scale)
     b = make_batch(dec, lengths=lens, seed=key + [_STREAM_PREFILL_POOL])
     T = int(n.sum())
     Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_size

@@ -31,6 +31,7 @@ def test_header_declares_expected_api():
                                   "pa_decode_partition_size", "pa_decode", "pa_cache_write_fp8",
                                   "pa_decode_fp8", "pa_decode_cascade",
                                   "pa_decode_cascade_workspace_size", "pa_prefill",
+                                  "pa_prefill_fp8",
                                   "pa_prefill_slot_mapping", "pa_pool_create",
                                   "pa_pool_destroy", "pa_pool_num_free", "pa_pool_ref_count",
                                   "pa_pool_allocate", "pa_pool_free", "pa_pool_share",
@@ -282,6 +283,29 @@ def test_prefill_validation(lib, kw, code):
     st = pa.load().pa_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["qs"], a["scale"],
                               a["out"], a["B"], a["T"], a["mq"], a["Hq"], a["Hkv"], a["D"],
                               a["bs"], a["NB"], a["MB"], a["maxlen"], a["dtype"], a["stream"])
+    assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), -2),
+    (dict(vs=-1.0), -2),
+    (dict(ks=float("inf")), -2),
+    (dict(vs=float("nan")), -2),
+    (dict(dtype=2), -3),
+    (dict(D=96), -4),
+    (dict(qs=None), -1),
+    (dict(B=0, ks=0.0), -2),             # the scales are checked before an empty call returns
+    (dict(B=0), 0),
+])
+def test_prefill_fp8_validation(lib, kw, code):
+    a = dict(q=16, kc=16, vc=16, bt=16, lens=16, qs=16, scale=0.125, ks=0.03125, vs=0.03125,
+             out=16, B=2, T=10, mq=8, Hq=4, Hkv=4, D=128, bs=16, NB=10, MB=4, maxlen=64, dtype=F,
+             stream=None)
+    a.update(kw)
+    st = pa.load().pa_prefill_fp8(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["qs"],
+                                  a["scale"], a["ks"], a["vs"], a["out"], a["B"], a["T"], a["mq"],
+                                  a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"],
+                                  a["maxlen"], a["dtype"], a["stream"])
     assert st == code
 
 

@@ -197,3 +197,29 @@ def test_copy_blocks_above_2g_elements():
         blk = int(pool.perm[c])
         assert np.array_equal(down16(pool.kc[blk]), kc[c])
         assert np.array_equal(down16(pool.vc[blk]), vc[c])
+
+
+def test_prefill_fp8_above_2g_bytes():
+    b = wl.make_prefill_batch(wl.PREFILL_CONFIGS["gqa_8b_chunked_prefill_fp8"], ctx=[900, 0, 129],
+                              new=[80, 300, 1])
+    pool = BigPool(b.key_cache, b.value_cache, b.block_tables, b.dtype, True, seed=88)
+    say(f"large pool prefill fp8 T={b.num_tokens} first block {pool.first}")
+    dt, ks, vs = b.dtype, float(b.k_scale), float(b.v_scale)
+    q, kn, vn = up16(b.q, dt), up16(b.k_new, dt), up16(b.v_new, dt)
+    lens, qs = up32(b.context_lens), up32(b.query_start)
+    bs = b.spec.block_size
+    slots = pa.prefill_slot_mapping(pool.bt, lens, qs, b.num_tokens, b.max_query_len, bs,
+                                    b.max_context_len)
+    pa.cache_write_fp8(kn, vn, pool.kc, pool.vc, slots, ks, vs)
+    out = pa.prefill_fp8(q, pool.kc, pool.vc, pool.bt, lens, qs, float(b.scale), ks, vs,
+                         b.max_query_len, b.max_context_len)
+    torch.cuda.synchronize()
+    ref_slots = oracle.prefill_slot_mapping(b.block_tables, b.context_lens, b.query_start, bs)
+    kc, vc = oracle.cache_write_fp8(b.key_cache, b.value_cache, b.k_new, b.v_new, ref_slots, dt,
+                                    ks, vs)
+    assert np.array_equal(pool.rows(pool.kc, ref_slots), kc[ref_slots // bs, ref_slots % bs])
+    ref = oracle.prefill(b.q, kc, vc, b.block_tables, b.context_lens, b.query_start, b.scale, dt,
+                         cache_dtype="fp8", k_scale=ks, v_scale=vs)
+    err = max_err(out, ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dt]
